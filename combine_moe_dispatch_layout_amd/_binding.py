@@ -1,0 +1,298 @@
+"""ctypes binding of libmoe_ep.so (include/moe_ep.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch provides device memory (torch.empty on the current device) and
+the stream (torch.cuda.current_stream()).  There is no fallback: if the library
+is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_ep.so")
+
+# ---------------------------------------------------------------- constants
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_CAPACITY = 3
+MOE_ERR_HANDLE = 4
+MOE_ERR_HIP = 5
+MOE_ERR_BAD_TOPK = 6
+MOE_ERR_DEVICE_BOUNDS = 7
+
+MOE_QUANT_BF16 = 0
+MOE_QUANT_FP8_E4M3 = 1
+MOE_LAYOUT_CONTIGUOUS = 0
+MOE_LAYOUT_PADDED_LL = 1
+
+(MOE_BUF_SEND_ROWS, MOE_BUF_SEND_SCALES, MOE_BUF_RECV_ROWS, MOE_BUF_RECV_SCALES, MOE_BUF_EXPERT_OUT,
+ MOE_BUF_COMBINE_OUT, MOE_BUF_HANDLE_POS, MOE_BUF_HANDLE_EXPERT_OFFSETS, MOE_BUF_HANDLE_RANK_OFFSETS,
+ MOE_BUF_HANDLE_SEND_SRC, MOE_BUF_HANDLE_RECV_SRC, MOE_BUF_HANDLE_RECV_COUNTS,
+ MOE_BUF_LAYOUT_EXPERT_COUNTS, MOE_BUF_LAYOUT_RANK_COUNTS, MOE_BUF_LAYOUT_TOKEN_IN_RANK,
+ MOE_BUF_WORKSPACE) = range(16)
+
+MOE_KERNEL_LAYOUT, MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE = 0, 1, 2
+KERNEL_NAMES = ("layout", "dispatch", "combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s" % (what, status_str(status)))
+
+
+# ---------------------------------------------------------------- C structs
+class moe_config(ctypes.Structure):
+    _fields_ = [("max_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("src_rank", ctypes.c_int32),
+                ("quant", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class moe_dispatch_buffers(ctypes.Structure):
+    _fields_ = [("send_rows", ctypes.c_void_p), ("send_scales", ctypes.c_void_p),
+                ("recv_rows", ctypes.c_void_p), ("recv_scales", ctypes.c_void_p)]
+
+
+class moe_handle(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("rank_offsets", ctypes.c_void_p), ("send_src_idx", ctypes.c_void_p),
+                ("recv_src_idx", ctypes.c_void_p), ("recv_counts", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int32), ("tag", ctypes.c_uint32)]
+
+
+# the full list of symbols include/moe_ep.h declares
+EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy", "moe_ctx_config",
+           "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_poll_error",
+           "moe_timing_begin", "moe_timing_end")
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Open libmoe_ep.so (raises if it has not been built) and declare the ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libmoe_ep.so is not built (%s); run `python __graft_entry__.py` "
+                           "or combine_moe_dispatch_layout_amd/_build.py" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, u32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint32)
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    sigs = {
+        "moe_size_hint": [ctypes.POINTER(moe_config), i32, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_ctx_create": [ctypes.POINTER(moe_config), ctypes.POINTER(vp)],
+        "moe_ctx_destroy": [vp],
+        "moe_ctx_config": [vp, ctypes.POINTER(moe_config)],
+        "moe_ctx_tune": [vp, i32, i32],
+        "moe_dispatch_layout": [vp, vp, i32, vp, vp, vp, vp],
+        "moe_dispatch": [vp, vp, vp, i32, i32, ctypes.POINTER(moe_dispatch_buffers),
+                         ctypes.POINTER(moe_handle), vp],
+        "moe_combine": [vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp],
+        "moe_poll_error": [vp, vp, u32p],
+        "moe_timing_begin": [vp, i32],
+        "moe_timing_end": [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load_library().moe_status_str(status).decode()
+
+
+def _check(status, what):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_config(max_tokens, hidden, num_experts, num_ranks, topk, src_rank=0,
+                quant=MOE_QUANT_BF16, layout=MOE_LAYOUT_CONTIGUOUS):
+    return moe_config(max_tokens, hidden, num_experts, num_ranks, topk, src_rank, quant, layout)
+
+
+def moe_size_hint(cfg, kind):
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_size_hint(ctypes.byref(cfg), kind, ctypes.byref(n)), "moe_size_hint")
+    return n.value
+
+
+# ---------------------------------------------------------------- context
+class Context:
+    """A moe_ctx on the current device, plus the configuration it was made with."""
+
+    def __init__(self, cfg):
+        lib = load_library()
+        self.cfg = cfg
+        h = ctypes.c_void_p(0)
+        _check(lib.moe_ctx_create(ctypes.byref(cfg), ctypes.byref(h)), "moe_ctx_create")
+        self._h = h
+        self.device = torch.cuda.current_device()
+
+    @property
+    def handle(self):
+        if self._h is None or not self._h.value:
+            raise RuntimeError("context already destroyed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(load_library().moe_ctx_destroy(self._h), "moe_ctx_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def hint(self, kind):
+        return moe_size_hint(self.cfg, kind)
+
+    def tune(self, dispatch_chunks=0, combine_chunks=0):
+        _check(load_library().moe_ctx_tune(self.handle, dispatch_chunks, combine_chunks), "moe_ctx_tune")
+
+    def timing_begin(self, max_launches):
+        _check(load_library().moe_timing_begin(self.handle, max_launches), "moe_timing_begin")
+
+    def timing_end(self):
+        tot = (ctypes.c_double * 3)()
+        cnt = (ctypes.c_int64 * 3)()
+        _check(load_library().moe_timing_end(self.handle, tot, cnt), "moe_timing_end")
+        return {KERNEL_NAMES[i]: {"total_ms": tot[i], "launches": cnt[i]} for i in range(3)}
+
+
+class Handle:
+    """Caller-owned device arrays of one dispatch (moe_handle), as torch tensors."""
+
+    def __init__(self, ctx):
+        c = ctx.cfg
+        dev = torch.device("cuda", ctx.device)
+        ksend = min(c.topk, c.num_ranks)
+        i32 = torch.int32
+        self.pos = torch.empty((c.max_tokens, c.topk), dtype=i32, device=dev)
+        self.expert_offsets = torch.empty(c.num_experts + 1, dtype=i32, device=dev)
+        self.rank_offsets = torch.empty(c.num_ranks + 1, dtype=i32, device=dev)
+        self.send_src_idx = torch.empty(c.max_tokens * ksend, dtype=i32, device=dev)
+        self.recv_src_idx = torch.empty(c.max_tokens * c.topk, dtype=i32, device=dev)
+        self.recv_counts = torch.empty(c.num_experts, dtype=i32, device=dev)
+        self.c = moe_handle(self.pos.data_ptr(), self.expert_offsets.data_ptr(),
+                            self.rank_offsets.data_ptr(), self.send_src_idx.data_ptr(),
+                            self.recv_src_idx.data_ptr(), self.recv_counts.data_ptr(), 0, 0)
+
+    @property
+    def num_tokens(self):
+        return self.c.num_tokens
+
+
+class DispatchBuffers:
+    """Caller-owned dispatch outputs sized by moe_size_hint (full capacity)."""
+
+    def __init__(self, ctx):
+        c = ctx.cfg
+        dev = torch.device("cuda", ctx.device)
+        fp8 = c.quant == MOE_QUANT_FP8_E4M3
+        ll = c.layout == MOE_LAYOUT_PADDED_LL
+        H = c.hidden
+        row_dt, row_w = (torch.uint8, H) if fp8 else (torch.bfloat16, H)
+        row_bytes = H if fp8 else 2 * H
+        n_send = ctx.hint(MOE_BUF_SEND_ROWS) // row_bytes
+        n_recv = ctx.hint(MOE_BUF_RECV_ROWS) // row_bytes
+        self.send_rows = None if ll else torch.empty((n_send, row_w), dtype=row_dt, device=dev)
+        self.send_scales = (torch.empty((n_send, H // 128), dtype=torch.float32, device=dev)
+                            if fp8 and not ll else None)
+        self.recv_rows = torch.empty((n_recv, row_w), dtype=row_dt, device=dev)
+        self.recv_scales = torch.empty((n_recv, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        self.c = moe_dispatch_buffers(_ptr(self.send_rows).value, _ptr(self.send_scales).value,
+                                      _ptr(self.recv_rows).value, _ptr(self.recv_scales).value)
+
+
+# ---------------------------------------------------------------- the calls
+def _as_dev(t, dtype, name):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+    return t
+
+
+def moe_dispatch_layout(ctx, topk_idx, num_tokens_per_expert=None, num_tokens_per_rank=None,
+                        is_token_in_rank=None):
+    """Returns (num_tokens_per_expert int32[E], num_tokens_per_rank int32[R],
+    is_token_in_rank uint8[T, R])."""
+    c = ctx.cfg
+    _as_dev(topk_idx, torch.int64, "topk_idx")
+    T = topk_idx.shape[0]
+    if topk_idx.dim() != 2 or topk_idx.shape[1] != c.topk:
+        raise ValueError("topk_idx must be [T, %d]" % c.topk)
+    dev = topk_idx.device
+    if num_tokens_per_expert is None:
+        num_tokens_per_expert = torch.empty(c.num_experts, dtype=torch.int32, device=dev)
+    if num_tokens_per_rank is None:
+        num_tokens_per_rank = torch.empty(c.num_ranks, dtype=torch.int32, device=dev)
+    if is_token_in_rank is None:
+        is_token_in_rank = torch.empty((T, c.num_ranks), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_dispatch_layout(
+        ctx.handle, _ptr(topk_idx), T, _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
+        _ptr(is_token_in_rank), _stream()), "moe_dispatch_layout")
+    return num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank
+
+
+def moe_dispatch(ctx, x, topk_idx, reuse_layout=False, bufs=None, handle=None):
+    """Returns (DispatchBuffers, Handle).  Pass preallocated bufs/handle to
+    avoid any allocation (e.g. inside timed loops)."""
+    c = ctx.cfg
+    _as_dev(x, torch.bfloat16, "x")
+    _as_dev(topk_idx, torch.int64, "topk_idx")
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != c.hidden or tuple(topk_idx.shape) != (T, c.topk):
+        raise ValueError("x must be [T, %d] and topk_idx [T, %d]" % (c.hidden, c.topk))
+    if bufs is None:
+        bufs = DispatchBuffers(ctx)
+    if handle is None:
+        handle = Handle(ctx)
+    _check(load_library().moe_dispatch(ctx.handle, _ptr(x), _ptr(topk_idx), T, int(bool(reuse_layout)),
+                                       ctypes.byref(bufs.c), ctypes.byref(handle.c), _stream()),
+           "moe_dispatch")
+    return bufs, handle
+
+
+def moe_combine(ctx, expert_out, topk_weights, handle, out=None):
+    """Returns out, bf16 [T, H]."""
+    c = ctx.cfg
+    _as_dev(expert_out, torch.bfloat16, "expert_out")
+    _as_dev(topk_weights, torch.float32, "topk_weights")
+    T = handle.num_tokens
+    if tuple(topk_weights.shape) != (T, c.topk):
+        raise ValueError("topk_weights must be [T, %d]" % c.topk)
+    if expert_out.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
+        raise ValueError("expert_out smaller than MOE_BUF_EXPERT_OUT")
+    if out is None:
+        out = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=expert_out.device)
+    _check(load_library().moe_combine(ctx.handle, _ptr(expert_out), _ptr(topk_weights),
+                                      ctypes.byref(handle.c), _ptr(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_poll_error(ctx):
+    """Synchronizes the current stream; returns (status, raw flags) and clears them."""
+    flags = ctypes.c_uint32(0)
+    st = load_library().moe_poll_error(ctx.handle, _stream(), ctypes.byref(flags))
+    if st not in (MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_DEVICE_BOUNDS):
+        raise MoeError(st, "moe_poll_error")
+    return st, flags.value

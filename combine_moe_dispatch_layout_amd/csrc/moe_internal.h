@@ -1,0 +1,88 @@
+// Internal declarations shared by the kernels (moe_kernels.hip) and the host
+// runtime (moe_runtime.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// One layout tile = 256 tokens = 4 wavefronts x 64 tokens (one token per lane).
+constexpr int kTileTokens = 256;
+constexpr int kBlockThreads = 256;
+constexpr int kWavesPerBlock = kBlockThreads / 64;
+
+// Bits of the sticky device error word.
+constexpr uint32_t kErrBadTopk = 1u;
+constexpr uint32_t kErrBounds = 2u;
+
+struct LayoutArgs {
+    const int64_t* topk_idx;   // [T, k]
+    int32_t T, k, E, R, El;
+    int32_t ebits, rbits;      // bits needed to hold an expert id / a rank id
+    int32_t max_tokens;        // row stride of srank
+    int32_t* tile_e;           // [ntiles, E]  per-tile counts -> global row bases
+    int32_t* tile_r;           // [ntiles, R]
+    uint16_t* erank;           // [T, k]       rank of slot (t, j) among its expert's rows in the tile
+    uint16_t* srank;           // [R, max_tokens] rank of token t among the tile's tokens sent to r
+    int32_t* cnt_e;            // [E]   workspace copies of the results
+    int32_t* cnt_r;            // [R]
+    int32_t* eoff;             // [E+1]
+    int32_t* roff;             // [R+1]
+    int32_t* out_cnt_e;        // nullable user outputs
+    int32_t* out_cnt_r;
+    uint8_t* out_in_rank;      // [T, R]
+    uint32_t* err;
+    uint32_t* done;            // arrival counter of the tile blocks (reset by the last one)
+};
+
+struct PackArgs {
+    const uint16_t* x;         // bf16 [T, H]
+    const int64_t* topk_idx;   // [T, k]
+    int32_t T, k, E, R, El, H;
+    int32_t rbits;
+    int32_t nslices;           // work items per token (row split)
+    int32_t max_tokens;
+    int32_t s0;
+    int64_t cap;               // low-latency slots per expert (M * R)
+    const int32_t* tile_e;
+    const int32_t* tile_r;
+    const uint16_t* erank;
+    const uint16_t* srank;
+    const int32_t* cnt_e;
+    const int32_t* eoff;
+    const int32_t* roff;
+    void* send_rows;
+    float* send_scales;
+    void* recv_rows;
+    float* recv_scales;
+    int64_t send_cap_rows;     // rows the send buffer holds
+    int64_t recv_cap_rows;     // rows the receive buffer holds
+    int64_t pairs_cap;         // entries of recv_src_idx (max_tokens * k)
+    int32_t* h_pos;
+    int32_t* h_eoff;
+    int32_t* h_roff;
+    int32_t* h_send_src;
+    int32_t* h_recv_src;
+    int32_t* h_recv_counts;
+    uint32_t* err;
+};
+
+struct CombineArgs {
+    const uint16_t* y;         // bf16 expert outputs in the receive layout
+    const float* w;            // [T, k]
+    const int32_t* pos;        // [T, k]
+    uint16_t* out;             // bf16 [T, H]
+    int32_t T, k, H;
+    int32_t nslices;
+    int64_t rows_cap;          // rows of y the caller's buffer holds
+    uint32_t* err;
+};
+
+// Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
+hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s);
+// chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16)
+hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,525 @@
+// Host runtime behind the C ABI in include/moe_ep.h: configuration checks,
+// buffer sizing, the context and its device workspace, launch geometry,
+// handle validation, the sticky device error word and optional kernel timing.
+//
+// Nothing here allocates after moe_ctx_create (the pages' "pre-allocation"
+// and "fixed-size buffers instead of queues": "DeepEP cross-node optimisation
+// guide", "Low-latency mode key features" and "Performance tuning").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "moe_ep.h"
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+using namespace moe;
+
+namespace {
+
+constexpr uint32_t kTagMagic = 0x4d6f4500u;   // "MoE\0"
+
+struct Geometry {
+    int El, ksend, ntiles_max, ebits, rbits;
+    int64_t cap, row_bytes, nb;
+    int64_t send_rows, recv_rows;
+};
+
+int bits_for(int n) {   // bits needed to hold values 0..n-1
+    int b = 0;
+    while ((1 << b) < n) ++b;
+    return b;
+}
+
+moe_status check_config(const moe_config* c, Geometry* g) {
+    if (c == nullptr) return MOE_ERR_INVALID_ARG;
+    if (c->max_tokens < 1 || c->hidden < 1 || c->num_experts < 1 || c->num_ranks < 1 || c->topk < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (c->src_rank < 0 || c->src_rank >= c->num_ranks) return MOE_ERR_INVALID_ARG;
+    if (c->quant != MOE_QUANT_BF16 && c->quant != MOE_QUANT_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (c->layout != MOE_LAYOUT_CONTIGUOUS && c->layout != MOE_LAYOUT_PADDED_LL) return MOE_ERR_INVALID_ARG;
+    if (c->num_experts > MOE_MAX_EXPERTS || c->num_ranks > MOE_MAX_RANKS || c->topk > MOE_MAX_TOPK ||
+        c->hidden > MOE_MAX_HIDDEN)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->num_experts % c->num_ranks != 0) return MOE_ERR_UNSUPPORTED;
+    if (c->hidden % (c->quant == MOE_QUANT_FP8_E4M3 ? 128 : 8) != 0) return MOE_ERR_UNSUPPORTED;
+    Geometry q;
+    q.El = c->num_experts / c->num_ranks;
+    q.ksend = std::min(c->topk, c->num_ranks);
+    q.ntiles_max = (c->max_tokens + kTileTokens - 1) / kTileTokens;
+    q.ebits = bits_for(c->num_experts);
+    q.rbits = bits_for(c->num_ranks);
+    q.cap = (int64_t)c->max_tokens * c->num_ranks;
+    q.row_bytes = c->quant == MOE_QUANT_FP8_E4M3 ? c->hidden : 2 * (int64_t)c->hidden;
+    q.nb = c->hidden / 128;
+    q.send_rows = c->layout == MOE_LAYOUT_PADDED_LL ? 0 : (int64_t)c->max_tokens * q.ksend;
+    q.recv_rows = c->layout == MOE_LAYOUT_PADDED_LL ? (int64_t)c->num_experts * q.cap
+                                                    : (int64_t)c->max_tokens * c->topk;
+    // row indices and flat (token, slot) indices are int32 on the device
+    if ((int64_t)c->max_tokens * c->topk >= INT32_MAX || q.recv_rows >= INT32_MAX ||
+        (int64_t)c->max_tokens * c->num_ranks >= INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    if (g) *g = q;
+    return MOE_OK;
+}
+
+// Workspace layout (device, one allocation, 256-byte aligned pieces).
+struct Workspace {
+    size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_e, off_tile_r,
+        off_erank, off_srank, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace plan_workspace(const moe_config* c, const Geometry& g) {
+    Workspace w;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    w.off_err = take(4);
+    w.off_done = take(4);
+    w.off_cnt_e = take(4 * (size_t)c->num_experts);
+    w.off_cnt_r = take(4 * (size_t)c->num_ranks);
+    w.off_eoff = take(4 * ((size_t)c->num_experts + 1));
+    w.off_roff = take(4 * ((size_t)c->num_ranks + 1));
+    w.off_tile_e = take(4 * (size_t)g.ntiles_max * c->num_experts);
+    w.off_tile_r = take(4 * (size_t)g.ntiles_max * c->num_ranks);
+    w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
+    w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
+    w.total = o;
+    return w;
+}
+
+uint32_t config_tag(const moe_config* c) {
+    uint32_t h = 2166136261u;   // FNV-1a over the config fields
+    const int32_t f[8] = {c->max_tokens, c->hidden, c->num_experts, c->num_ranks,
+                          c->topk, c->src_rank, c->quant, c->layout};
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(f);
+    for (size_t i = 0; i < sizeof(f); ++i) h = (h ^ b[i]) * 16777619u;
+    return (h & 0xffffff00u) ^ kTagMagic;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest power-of-two chunk count per lane not above `need` (1..16).
+int pow2_floor16(int64_t need) {
+    int c = 1;
+    while (c < 16 && (int64_t)c * 2 <= need) c *= 2;
+    return c;
+}
+
+// Work split of a row-streaming kernel: each wavefront handles `chunks`
+// 16-byte chunks per lane of one token row (a "slice").  Whole rows per
+// wavefront when there are enough tokens to fill the chip; otherwise rows are
+// cut into more slices so that at least ~8 wavefronts per CU are in flight.
+void row_split(int64_t T, int64_t nchunk, int forced, int* chunks, int* nslices) {
+    int c;
+    if (forced > 0) {
+        c = forced;
+    } else {
+        const int64_t per_lane = (nchunk + 63) / 64;
+        c = 1;
+        while (c < 16 && c < per_lane) c *= 2;                   // ceil to pow2, whole row
+        const int64_t target_items = 256 * 8;                    // 8 wavefronts per CU
+        while (c > 1 && T * ((nchunk + 64 * c - 1) / (64 * c)) < target_items) c /= 2;
+    }
+    *chunks = c;
+    *nslices = (int)((nchunk + 64 * c - 1) / (64 * c));
+}
+
+}  // namespace
+
+struct moe_ctx {
+    moe_config cfg;
+    Geometry g;
+    Workspace wl;
+    int device;
+    char* ws;
+    uint32_t tag;
+    // last layout computed into the workspace
+    const int64_t* layout_idx;
+    int32_t layout_T;
+    bool layout_valid;
+    // tuning overrides (0 = heuristic)
+    int pack_chunks, combine_chunks;
+    // timing
+    bool timing;
+    int max_launches;
+    std::vector<hipEvent_t> ev0, ev1;
+    std::vector<int> kid;
+
+    uint32_t* err() { return reinterpret_cast<uint32_t*>(ws + wl.off_err); }
+    uint32_t* done() { return reinterpret_cast<uint32_t*>(ws + wl.off_done); }
+    int32_t* i32(size_t off) { return reinterpret_cast<int32_t*>(ws + off); }
+    uint16_t* u16(size_t off) { return reinterpret_cast<uint16_t*>(ws + off); }
+};
+
+namespace {
+
+bool on_ctx_device(const moe_ctx* ctx) {
+    int dev = -1;
+    return hipGetDevice(&dev) == hipSuccess && dev == ctx->device;
+}
+
+// Record timing events around one launch when timing is on.
+struct TimedLaunch {
+    moe_ctx* ctx;
+    hipStream_t s;
+    int slot;
+    TimedLaunch(moe_ctx* c, hipStream_t st, int id) : ctx(c), s(st), slot(-1) {
+        if (c->timing && (int)c->kid.size() < c->max_launches) {
+            slot = (int)c->kid.size();
+            c->kid.push_back(id);
+            (void)hipEventRecord(c->ev0[slot], st);
+        }
+    }
+    void done() {
+        if (slot >= 0) (void)hipEventRecord(ctx->ev1[slot], s);
+    }
+};
+
+moe_status run_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t T, int32_t* out_cnt_e,
+                      int32_t* out_cnt_r, uint8_t* out_in_rank, hipStream_t s) {
+    const moe_config& c = ctx->cfg;
+    LayoutArgs a;
+    a.topk_idx = topk_idx;
+    a.T = T;
+    a.k = c.topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.El = ctx->g.El;
+    a.ebits = ctx->g.ebits;
+    a.rbits = ctx->g.rbits;
+    a.max_tokens = c.max_tokens;
+    a.tile_e = ctx->i32(ctx->wl.off_tile_e);
+    a.tile_r = ctx->i32(ctx->wl.off_tile_r);
+    a.erank = ctx->u16(ctx->wl.off_erank);
+    a.srank = ctx->u16(ctx->wl.off_srank);
+    a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
+    a.cnt_r = ctx->i32(ctx->wl.off_cnt_r);
+    a.eoff = ctx->i32(ctx->wl.off_eoff);
+    a.roff = ctx->i32(ctx->wl.off_roff);
+    a.out_cnt_e = out_cnt_e;
+    a.out_cnt_r = out_cnt_r;
+    a.out_in_rank = out_in_rank;
+    a.err = ctx->err();
+    a.done = ctx->done();
+    const int ntiles = std::max(1, (T + kTileTokens - 1) / kTileTokens);
+    TimedLaunch tl(ctx, s, MOE_KERNEL_LAYOUT);
+    hipError_t e = launch_layout(a, ntiles, s);
+    tl.done();
+    if (e != hipSuccess) {
+        ctx->layout_valid = false;
+        return MOE_ERR_HIP;
+    }
+    ctx->layout_idx = topk_idx;
+    ctx->layout_T = T;
+    ctx->layout_valid = true;
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ============================================================== C ABI
+MOE_API const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY";
+        case MOE_ERR_HANDLE: return "MOE_ERR_HANDLE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        case MOE_ERR_BAD_TOPK: return "MOE_ERR_BAD_TOPK";
+        case MOE_ERR_DEVICE_BOUNDS: return "MOE_ERR_DEVICE_BOUNDS";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+MOE_API moe_status moe_size_hint(const moe_config* cfg, int32_t kind, size_t* bytes) {
+    if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+    *bytes = 0;
+    Geometry g;
+    moe_status st = check_config(cfg, &g);
+    if (st != MOE_OK) return st;
+    const bool fp8 = cfg->quant == MOE_QUANT_FP8_E4M3;
+    const bool ll = cfg->layout == MOE_LAYOUT_PADDED_LL;
+    const size_t M = (size_t)cfg->max_tokens, E = (size_t)cfg->num_experts, R = (size_t)cfg->num_ranks,
+                 k = (size_t)cfg->topk, H = (size_t)cfg->hidden;
+    switch (kind) {
+        case MOE_BUF_SEND_ROWS: *bytes = (size_t)g.send_rows * g.row_bytes; break;
+        case MOE_BUF_SEND_SCALES: *bytes = fp8 && !ll ? (size_t)g.send_rows * g.nb * 4 : 0; break;
+        case MOE_BUF_RECV_ROWS: *bytes = (size_t)g.recv_rows * g.row_bytes; break;
+        case MOE_BUF_RECV_SCALES: *bytes = fp8 ? (size_t)g.recv_rows * g.nb * 4 : 0; break;
+        case MOE_BUF_EXPERT_OUT: *bytes = (size_t)g.recv_rows * H * 2; break;
+        case MOE_BUF_COMBINE_OUT: *bytes = M * H * 2; break;
+        case MOE_BUF_HANDLE_POS: *bytes = M * k * 4; break;
+        case MOE_BUF_HANDLE_EXPERT_OFFSETS: *bytes = (E + 1) * 4; break;
+        case MOE_BUF_HANDLE_RANK_OFFSETS: *bytes = (R + 1) * 4; break;
+        case MOE_BUF_HANDLE_SEND_SRC: *bytes = M * (size_t)g.ksend * 4; break;
+        case MOE_BUF_HANDLE_RECV_SRC: *bytes = M * k * 4; break;
+        case MOE_BUF_HANDLE_RECV_COUNTS: *bytes = E * 4; break;
+        case MOE_BUF_LAYOUT_EXPERT_COUNTS: *bytes = E * 4; break;
+        case MOE_BUF_LAYOUT_RANK_COUNTS: *bytes = R * 4; break;
+        case MOE_BUF_LAYOUT_TOKEN_IN_RANK: *bytes = M * R; break;
+        case MOE_BUF_WORKSPACE: *bytes = plan_workspace(cfg, g).total; break;
+        default: return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out) {
+    if (out == nullptr) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    Geometry g;
+    moe_status st = check_config(cfg, &g);
+    if (st != MOE_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    moe_ctx* ctx = new (std::nothrow) moe_ctx();
+    if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+    ctx->cfg = *cfg;
+    ctx->g = g;
+    ctx->wl = plan_workspace(cfg, g);
+    ctx->device = dev;
+    ctx->ws = nullptr;
+    ctx->tag = config_tag(cfg);
+    ctx->layout_idx = nullptr;
+    ctx->layout_T = -1;
+    ctx->layout_valid = false;
+    ctx->pack_chunks = 0;
+    ctx->combine_chunks = 0;
+    ctx->timing = false;
+    ctx->max_launches = 0;
+    if (hipMalloc(reinterpret_cast<void**>(&ctx->ws), ctx->wl.total) != hipSuccess) {
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    // error word and arrival counter start at zero; the rest is written before it is read
+    if (hipMemset(ctx->ws, 0, 256 * 2) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(ctx->ws);
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    *out = ctx;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_ctx_destroy(moe_ctx* ctx) {
+    if (ctx == nullptr) return MOE_OK;
+    moe_status st = MOE_OK;
+    if (hipDeviceSynchronize() != hipSuccess) st = MOE_ERR_HIP;
+    for (hipEvent_t e : ctx->ev0) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ctx->ev1) (void)hipEventDestroy(e);
+    if (ctx->ws && hipFree(ctx->ws) != hipSuccess) st = MOE_ERR_HIP;
+    delete ctx;
+    return st;
+}
+
+MOE_API moe_status moe_ctx_config(const moe_ctx* ctx, moe_config* out) {
+    if (ctx == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+    *out = ctx->cfg;
+    return MOE_OK;
+}
+
+// Tuning override for sweeps: chunks per lane of the dispatch / combine kernels
+// (0 = heuristic; else 1, 2, 4, 8 or 16).  Not in the public header.
+MOE_API moe_status moe_ctx_tune(moe_ctx* ctx, int32_t pack_chunks, int32_t combine_chunks) {
+    if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+    auto ok = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8 || v == 16; };
+    if (!ok(pack_chunks) || !ok(combine_chunks)) return MOE_ERR_INVALID_ARG;
+    ctx->pack_chunks = pack_chunks;
+    ctx->combine_chunks = combine_chunks;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
+                                       int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank,
+                                       uint8_t* is_token_in_rank, void* stream) {
+    if (ctx == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (num_tokens > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens > 0 && topk_idx == nullptr) return MOE_ERR_INVALID_ARG;
+    return run_layout(ctx, topk_idx, num_tokens, num_tokens_per_expert, num_tokens_per_rank,
+                      is_token_in_rank, reinterpret_cast<hipStream_t>(stream));
+}
+
+MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, int32_t num_tokens,
+                                int32_t reuse_layout, const moe_dispatch_buffers* bufs, moe_handle* handle,
+                                void* stream) {
+    if (ctx == nullptr || bufs == nullptr || handle == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    const bool fp8 = c.quant == MOE_QUANT_FP8_E4M3;
+    const bool ll = c.layout == MOE_LAYOUT_PADDED_LL;
+    if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens > 0 && (x == nullptr || topk_idx == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (bufs->recv_rows == nullptr || !aligned16(x) || !aligned16(bufs->recv_rows)) return MOE_ERR_INVALID_ARG;
+    if (ll) {
+        if (bufs->send_rows != nullptr || bufs->send_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (bufs->send_rows == nullptr || !aligned16(bufs->send_rows)) return MOE_ERR_INVALID_ARG;
+        if (fp8 != (bufs->send_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    }
+    if (fp8 != (bufs->recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (handle->pos == nullptr || handle->expert_offsets == nullptr || handle->rank_offsets == nullptr ||
+        handle->send_src_idx == nullptr || handle->recv_src_idx == nullptr || handle->recv_counts == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (reuse_layout != 0 && reuse_layout != 1) return MOE_ERR_INVALID_ARG;
+    if (reuse_layout && (!ctx->layout_valid || ctx->layout_idx != topk_idx || ctx->layout_T != num_tokens))
+        return MOE_ERR_INVALID_ARG;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!reuse_layout) {
+        moe_status st = run_layout(ctx, topk_idx, num_tokens, nullptr, nullptr, nullptr, s);
+        if (st != MOE_OK) return st;
+    }
+
+    PackArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.topk_idx = topk_idx;
+    a.T = num_tokens;
+    a.k = c.topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.El = ctx->g.El;
+    a.H = c.hidden;
+    a.rbits = ctx->g.rbits;
+    a.max_tokens = c.max_tokens;
+    a.s0 = c.src_rank;
+    a.cap = ctx->g.cap;
+    a.tile_e = ctx->i32(ctx->wl.off_tile_e);
+    a.tile_r = ctx->i32(ctx->wl.off_tile_r);
+    a.erank = ctx->u16(ctx->wl.off_erank);
+    a.srank = ctx->u16(ctx->wl.off_srank);
+    a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
+    a.eoff = ctx->i32(ctx->wl.off_eoff);
+    a.roff = ctx->i32(ctx->wl.off_roff);
+    a.send_rows = bufs->send_rows;
+    a.send_scales = bufs->send_scales;
+    a.recv_rows = bufs->recv_rows;
+    a.recv_scales = bufs->recv_scales;
+    a.send_cap_rows = ctx->g.send_rows;
+    a.recv_cap_rows = ctx->g.recv_rows;
+    a.pairs_cap = (int64_t)c.max_tokens * c.topk;
+    a.h_pos = handle->pos;
+    a.h_eoff = handle->expert_offsets;
+    a.h_roff = handle->rank_offsets;
+    a.h_send_src = handle->send_src_idx;
+    a.h_recv_src = handle->recv_src_idx;
+    a.h_recv_counts = handle->recv_counts;
+    a.err = ctx->err();
+    int chunks, nslices;
+    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, &chunks, &nslices);
+    a.nslices = nslices;
+    // at least one block so that the handle's offsets and counts are written for T = 0
+    PackArgs a0 = a;
+    if (num_tokens == 0) a0.T = 0;
+    TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH);
+    hipError_t e;
+    if (num_tokens == 0) {
+        // grid of one block: block 0 copies the offsets, every wave exits (no items)
+        a0.nslices = 1;
+        e = launch_pack(a0, 1, fp8, ll, !ll, s);
+    } else {
+        e = launch_pack(a, chunks, fp8, ll, !ll, s);
+    }
+    tl.done();
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    handle->num_tokens = num_tokens;
+    handle->tag = ctx->tag;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float* topk_weights,
+                               const moe_handle* handle, void* out, void* stream) {
+    if (ctx == nullptr || handle == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (handle->tag != ctx->tag || handle->num_tokens < 0 || handle->num_tokens > c.max_tokens ||
+        handle->pos == nullptr)
+        return MOE_ERR_HANDLE;
+    const int32_t T = handle->num_tokens;
+    if (T == 0) return MOE_OK;
+    if (expert_out == nullptr || topk_weights == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(expert_out) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    CombineArgs a;
+    a.y = static_cast<const uint16_t*>(expert_out);
+    a.w = topk_weights;
+    a.pos = handle->pos;
+    a.out = static_cast<uint16_t*>(out);
+    a.T = T;
+    a.k = c.topk;
+    a.H = c.hidden;
+    a.rows_cap = ctx->g.recv_rows;
+    a.err = ctx->err();
+    int chunks, nslices;
+    row_split(T, c.hidden / 8, ctx->combine_chunks, &chunks, &nslices);
+    a.nslices = nslices;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE);
+    hipError_t e = launch_combine(a, chunks, c.topk, s);
+    tl.done();
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags) {
+    if (ctx == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipMemcpy(&v, ctx->err(), 4, hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+    if (v != 0 && hipMemset(ctx->err(), 0, 4) != hipSuccess) return MOE_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+    if (flags) *flags = v;
+    if (v & kErrBadTopk) return MOE_ERR_BAD_TOPK;
+    if (v & kErrBounds) return MOE_ERR_DEVICE_BOUNDS;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches) {
+    if (ctx == nullptr || max_launches < 1 || ctx->timing) return MOE_ERR_INVALID_ARG;
+    ctx->ev0.resize(max_launches);
+    ctx->ev1.resize(max_launches);
+    for (int i = 0; i < max_launches; ++i) {
+        if (hipEventCreate(&ctx->ev0[i]) != hipSuccess || hipEventCreate(&ctx->ev1[i]) != hipSuccess) {
+            return MOE_ERR_HIP;
+        }
+    }
+    ctx->kid.clear();
+    ctx->kid.reserve(max_launches);
+    ctx->max_launches = max_launches;
+    ctx->timing = true;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches) {
+    if (ctx == nullptr || !ctx->timing) return MOE_ERR_INVALID_ARG;
+    moe_status st = MOE_OK;
+    double tot[MOE_KERNEL_COUNT] = {0, 0, 0};
+    int64_t cnt[MOE_KERNEL_COUNT] = {0, 0, 0};
+    for (size_t i = 0; i < ctx->kid.size(); ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(ctx->ev1[i]) != hipSuccess ||
+            hipEventElapsedTime(&ms, ctx->ev0[i], ctx->ev1[i]) != hipSuccess) {
+            st = MOE_ERR_HIP;
+            break;
+        }
+        tot[ctx->kid[i]] += ms;
+        cnt[ctx->kid[i]] += 1;
+    }
+    for (hipEvent_t e : ctx->ev0) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ctx->ev1) (void)hipEventDestroy(e);
+    ctx->ev0.clear();
+    ctx->ev1.clear();
+    ctx->kid.clear();
+    ctx->timing = false;
+    for (int i = 0; i < MOE_KERNEL_COUNT; ++i) {
+        if (total_ms) total_ms[i] = tot[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return st;
+}

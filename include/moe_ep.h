@@ -1,0 +1,264 @@
+/*
+ * moe_ep.h -- C ABI of libmoe_ep.so: MoE token dispatch-layout, dispatch and
+ * combine for one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the pages describe it in prose only):
+ *  - "DeepEP cross-node optimisation guide" (cyqw.cn), opening paragraph: the
+ *    all-to-all GPU kernels of an expert-parallel MoE library are "dispatch"
+ *    (send each token's hidden vector to the experts its router picked) and
+ *    "combine" (bring the expert outputs back and reduce them), with FP8
+ *    support.
+ *  - Same page, "Core API example": dispatch takes hidden_states, topk_idx,
+ *    num_max_dispatch_tokens_per_rank and num_experts; combine takes the expert
+ *    outputs, topk_weights and the handle returned by dispatch.
+ *  - Same page, figure caption in "Technical analysis": the layout (per-expert
+ *    and per-rank counts, token->rank map) is computed once and reused.
+ *  - Same page, "Low-latency mode key features" and "Performance tuning":
+ *    buffers are preallocated (with a size-hint call) and fixed-size, so no
+ *    allocation happens at run time.
+ *  - DeepTech release article on DeepEP (010bt.com), paragraph defining EP:
+ *    different experts live on different ranks.  Here expert e lives on
+ *    virtual rank e / (E / R).
+ * With a single GPU the transfer to peer ranks is a local copy: dispatch
+ * writes the per-destination-rank send buffers and the receive layout the
+ * experts read, combine reads expert outputs from that receive layout.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller allocates
+ *    and owns every buffer passed in or out (size them with moe_size_hint:
+ *    all sizes are static upper bounds, so no call ever needs a host sync).
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *    data-path call only enqueues work on that stream and returns; it never
+ *    blocks and never allocates device memory.
+ *  - A context is bound to the HIP device current at moe_ctx_create and to
+ *    one stream at a time; it is not thread-safe.  Calls made on another
+ *    device return MOE_ERR_INVALID_ARG.
+ *  - Argument errors are reported synchronously by the return value and leave
+ *    nothing enqueued.  Data errors found by the kernels (an expert id outside
+ *    [-1, E)) are recorded in a sticky device word that moe_poll_error reads;
+ *    the offending slot is then treated as empty (-1).
+ *  - bf16 buffers are passed as raw 16-bit storage; fp8 buffers hold OCP
+ *    E4M3FN codes, one byte per channel.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_EP_ABI_VERSION 1
+
+/* ---------------------------------------------------------------- status */
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, wrong device, bad config value */
+    MOE_ERR_UNSUPPORTED = 2,   /* outside the supported limits below */
+    MOE_ERR_CAPACITY = 3,      /* num_tokens > max_tokens (low-latency: > capacity per source rank) */
+    MOE_ERR_HANDLE = 4,        /* handle not produced by moe_dispatch on a compatible context */
+    MOE_ERR_HIP = 5,           /* a HIP runtime call failed */
+    MOE_ERR_BAD_TOPK = 6,      /* from moe_poll_error: an expert id outside [-1, E) was seen */
+    MOE_ERR_DEVICE_BOUNDS = 7  /* from moe_poll_error: a computed row fell outside its buffer
+                                  (topk_idx changed between moe_dispatch_layout and a
+                                  moe_dispatch that reused its layout); the row was dropped */
+} moe_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(moe_status s);
+
+/* ---------------------------------------------------------------- config */
+typedef enum moe_quant {
+    MOE_QUANT_BF16 = 0,        /* payload rows are the bf16 input rows */
+    MOE_QUANT_FP8_E4M3 = 1     /* payload rows are E4M3FN codes + one fp32 dequant scale
+                                  per 128 channels (kdjingpai.com DeepEP tutorial,
+                                  "Function 3: FP8 operation optimisation"; guide,
+                                  production setting "FP8 dispatch") */
+} moe_quant;
+
+typedef enum moe_layout {
+    MOE_LAYOUT_CONTIGUOUS = 0, /* normal (high-throughput) mode: packed rank-major send
+                                  buffer + contiguous expert-major receive rows */
+    MOE_LAYOUT_PADDED_LL = 1   /* low-latency mode: fixed slots, receive buffer
+                                  [R][E/R][max_tokens*R][row], no send buffer */
+} moe_layout;
+
+/* Supported limits (checked by moe_ctx_create / moe_size_hint). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_RANKS   64
+#define MOE_MAX_TOPK    32
+#define MOE_MAX_HIDDEN  32768
+
+typedef struct moe_config {
+    int32_t max_tokens;   /* M >= 1: upper bound on num_tokens of every call; in
+                             MOE_LAYOUT_PADDED_LL it is also the per-source-rank slot
+                             capacity (the pages' num_max_dispatch_tokens_per_rank) */
+    int32_t hidden;       /* H: channels per token; multiple of 8 (bf16), of 128 (fp8) */
+    int32_t num_experts;  /* E, 1..MOE_MAX_EXPERTS, multiple of num_ranks */
+    int32_t num_ranks;    /* R, 1..MOE_MAX_RANKS: virtual EP ranks; expert e -> rank e/(E/R) */
+    int32_t topk;         /* k, 1..MOE_MAX_TOPK: slots per token in topk_idx */
+    int32_t src_rank;     /* s0 in [0, R): this GPU's rank (selects its low-latency slots) */
+    int32_t quant;        /* moe_quant */
+    int32_t layout;       /* moe_layout */
+} moe_config;
+
+/* ---------------------------------------------------------------- sizes */
+typedef enum moe_buffer_kind {
+    MOE_BUF_SEND_ROWS = 0,      /* [max_tokens*min(k,R), row_bytes]; 0 in PADDED_LL */
+    MOE_BUF_SEND_SCALES = 1,    /* fp32 [max_tokens*min(k,R), H/128]; 0 unless fp8 and CONTIGUOUS */
+    MOE_BUF_RECV_ROWS = 2,      /* CONTIGUOUS: [max_tokens*k, row_bytes];
+                                   PADDED_LL: [E, max_tokens*R, row_bytes] */
+    MOE_BUF_RECV_SCALES = 3,    /* fp32, same row count as RECV_ROWS, H/128 per row; 0 for bf16 */
+    MOE_BUF_EXPERT_OUT = 4,     /* bf16 expert outputs read by combine: RECV_ROWS' row count x 2H */
+    MOE_BUF_COMBINE_OUT = 5,    /* bf16 [max_tokens, H] */
+    MOE_BUF_HANDLE_POS = 6,     /* int32 [max_tokens, k] */
+    MOE_BUF_HANDLE_EXPERT_OFFSETS = 7,  /* int32 [E+1] */
+    MOE_BUF_HANDLE_RANK_OFFSETS = 8,    /* int32 [R+1] */
+    MOE_BUF_HANDLE_SEND_SRC = 9,        /* int32 [max_tokens*min(k,R)] */
+    MOE_BUF_HANDLE_RECV_SRC = 10,       /* int32 [max_tokens*k] */
+    MOE_BUF_HANDLE_RECV_COUNTS = 11,    /* int32 [E] */
+    MOE_BUF_LAYOUT_EXPERT_COUNTS = 12,  /* int32 [E] */
+    MOE_BUF_LAYOUT_RANK_COUNTS = 13,    /* int32 [R] */
+    MOE_BUF_LAYOUT_TOKEN_IN_RANK = 14,  /* uint8 [max_tokens, R] */
+    MOE_BUF_WORKSPACE = 15,             /* device scratch the context allocates itself */
+    MOE_BUF_KIND_COUNT = 16
+} moe_buffer_kind;
+
+/* Bytes needed for one buffer kind under `cfg` (host pointers).  Pure host
+ * computation; needs no GPU.  Returns MOE_ERR_INVALID_ARG / UNSUPPORTED for a
+ * bad config or kind. */
+moe_status moe_size_hint(const moe_config* cfg, int32_t kind, size_t* bytes);
+
+/* ---------------------------------------------------------------- context */
+typedef struct moe_ctx moe_ctx;
+
+/* Validate `cfg` (host) and allocate the context and its device workspace
+ * (per-tile histograms and scan state, within-tile ranks, error word) on the
+ * current HIP device.  The only call that allocates.  On error *out is NULL. */
+moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out);
+
+/* Free the context.  Synchronizes the device first.  NULL is a no-op. */
+moe_status moe_ctx_destroy(moe_ctx* ctx);
+
+/* Copy of the configuration the context was created with (host). */
+moe_status moe_ctx_config(const moe_ctx* ctx, moe_config* out);
+
+/* Launch-geometry override, for measurement sweeps: 16-byte chunks each lane
+ * moves per work item in the dispatch and combine kernels (1, 2, 4, 8 or 16;
+ * 0 = the built-in choice, which keeps whole rows per wavefront when there
+ * are enough tokens to fill the chip and splits rows otherwise).  Results do
+ * not depend on it. */
+moe_status moe_ctx_tune(moe_ctx* ctx, int32_t dispatch_chunks, int32_t combine_chunks);
+
+/* ---------------------------------------------------------------- layout */
+/* Dispatch layout (guide, figure caption in "Technical analysis": computed once,
+ * reused by dispatch and combine).
+ *   topk_idx               int64 [num_tokens, k], row-major; -1 = empty slot
+ *   num_tokens_per_expert  int32 [E]:  valid slots routed to expert e
+ *   num_tokens_per_rank    int32 [R]:  tokens with at least one expert on rank r
+ *   is_token_in_rank       uint8 [num_tokens, R]: 1 iff token t goes to rank r
+ * Any output pointer may be NULL (not written).  0 <= num_tokens <= max_tokens.
+ * Also keeps, in the context's workspace, the scan state a following
+ * moe_dispatch(..., reuse_layout = 1) consumes. */
+moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
+                               int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank,
+                               uint8_t* is_token_in_rank, void* stream);
+
+/* ---------------------------------------------------------------- dispatch */
+/* Output buffers of one dispatch (host struct of device pointers).
+ * row_bytes = 2H (bf16) or H (fp8).  Row order:
+ *   send:  rank-major; rows [rank_offsets[r], rank_offsets[r+1]) go to rank r,
+ *          ascending token index inside each rank.
+ *   recv:  CONTIGUOUS: expert-major, rows [expert_offsets[e], expert_offsets[e+1])
+ *          for expert e, ordered by (token, slot);
+ *          PADDED_LL: row e*cap + s0*M + i (cap = M*R) holds the i-th token
+ *          routed to expert e; other slots are never written.
+ * Scales (fp8 only) are fp32 [rows, H/128], row-parallel to the data rows. */
+typedef struct moe_dispatch_buffers {
+    void*  send_rows;     /* CONTIGUOUS: required; PADDED_LL: must be NULL */
+    float* send_scales;   /* fp8 + CONTIGUOUS: required; else NULL */
+    void*  recv_rows;     /* required */
+    float* recv_scales;   /* fp8: required; else NULL */
+} moe_dispatch_buffers;
+
+/* Routing record written by moe_dispatch and read by moe_combine (host struct
+ * of caller-owned device buffers, sized by the MOE_BUF_HANDLE_* hints).
+ *   pos[t, j]        row of slot j of token t in the receive layout
+ *                    (CONTIGUOUS: expert-major row; PADDED_LL: e*cap + slot),
+ *                    -1 for an empty slot
+ *   expert_offsets   exclusive prefix sum of the per-expert counts (E+1)
+ *   rank_offsets     exclusive prefix sum of the per-rank token counts (R+1)
+ *   send_src_idx[i]  token of send row i (rank_offsets[R] entries)
+ *   recv_src_idx[i]  token of expert-major row i (expert_offsets[E] entries;
+ *                    in PADDED_LL the i-th row of expert e is slot s0*M + i -
+ *                    expert_offsets[e])
+ *   recv_counts[e]   rows received by expert e
+ * num_tokens and tag are written by moe_dispatch (host) and checked by
+ * moe_combine. */
+typedef struct moe_handle {
+    int32_t* pos;
+    int32_t* expert_offsets;
+    int32_t* rank_offsets;
+    int32_t* send_src_idx;
+    int32_t* recv_src_idx;
+    int32_t* recv_counts;
+    int32_t  num_tokens;
+    uint32_t tag;
+} moe_handle;
+
+/* MoE dispatch (guide, "Core API example"; DeepTech article, feature list).
+ *   x          bf16 [num_tokens, H] token hidden states
+ *   topk_idx   int64 [num_tokens, k]; -1 = empty slot
+ *   reuse_layout  0: compute the layout first (one extra kernel);
+ *                 1: reuse the scan state of the last moe_dispatch_layout on this
+ *                    context, which must have seen the same topk_idx pointer and
+ *                    num_tokens (checked; the contents must not have changed)
+ *   bufs       output rows (and scales for fp8)
+ *   handle     host struct; its device arrays are written, num_tokens/tag set
+ * fp8 rows: per token and 128-channel block, a = max|x|, a' = max(a, 1e-4),
+ * codes = E4M3(x * (448/a')) with round-to-nearest-even (saturating), stored
+ * scale = a'/448.  Every destination gets the same bytes. */
+moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, int32_t num_tokens,
+                        int32_t reuse_layout, const moe_dispatch_buffers* bufs,
+                        moe_handle* handle, void* stream);
+
+/* ---------------------------------------------------------------- combine */
+/* MoE combine (guide, "Core API example" and the production setting's
+ * "BF16 combine").
+ *   expert_out   bf16 rows in the receive layout of the handle (row pos[t, j])
+ *   topk_weights fp32 [num_tokens, k]
+ *   out          bf16 [num_tokens, H]
+ * out[t, h] = bf16_rne( sum over valid j, ascending, of w[t, j] * y[pos[t, j], h] ),
+ * accumulated in fp32 from +0 with separately rounded multiply and add. */
+moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float* topk_weights,
+                       const moe_handle* handle, void* out, void* stream);
+
+/* ---------------------------------------------------------------- errors */
+/* Synchronize `stream`, read and clear the sticky device error word.
+ * Returns MOE_OK, MOE_ERR_BAD_TOPK or MOE_ERR_DEVICE_BOUNDS (the first set,
+ * in that order); *flags (host, may be NULL) receives the raw bits. */
+moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags);
+
+/* ---------------------------------------------------------------- timing */
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * kernel the context enqueues.  Off by default.  moe_timing_begin allocates
+ * `max_launches` event pairs (host-side HIP objects, not device memory);
+ * moe_timing_end synchronizes on the last event, writes per-kernel totals
+ * (milliseconds) and launch counts (host arrays of MOE_KERNEL_COUNT entries)
+ * and frees the events.  Launches beyond max_launches are not timed. */
+typedef enum moe_kernel_id {
+    MOE_KERNEL_LAYOUT = 0,   /* count + scan */
+    MOE_KERNEL_DISPATCH = 1, /* pack / permute / quantise */
+    MOE_KERNEL_COMBINE = 2,  /* gather-reduce */
+    MOE_KERNEL_COUNT = 3
+} moe_kernel_id;
+
+moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches);
+moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_EP_H */

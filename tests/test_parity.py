@@ -1,0 +1,353 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: bit-exact for counts, offsets, positions, source indices, token->rank map,
+payload rows (bf16 bytes, fp8 codes and fp32 scales); combine within one bf16
+ulp (the kernel also uses separately rounded multiply and add, so it is
+expected -- and checked separately -- to be bit-exact).  Output buffers are
+poisoned first so stray or missing writes show up; combine inputs outside the
+routed rows are NaN so a wrong read shows up.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0xA5
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def bits_of(t):
+    """Device tensor -> host numpy array of raw bit patterns."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def make_ctx(gpu, c, T, max_tokens=None, src_rank=0):
+    M = max_tokens if max_tokens is not None else max(c["max_tokens"], T, 1)
+    cfg = gpu.make_config(M, c["H"], c["E"], c["R"], c["k"], src_rank, c["quant"], c["layout"])
+    return gpu.Context(cfg)
+
+
+def poison(bufs):
+    for t in (bufs.send_rows, bufs.recv_rows, bufs.send_scales, bufs.recv_scales):
+        if t is not None:
+            t.view(torch.uint8).fill_(POISON)
+
+
+def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, check_poison=True,
+             tag=""):
+    """Layout + dispatch + combine on the GPU and in the oracle; compare all."""
+    T = idx.shape[0]
+    ll = c["layout"] == W.LAYOUT_PADDED_LL
+    fp8 = c["quant"] == W.QUANT_FP8
+    log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d" %
+        (tag, T, c["H"], c["E"], c["R"], c["k"], c["quant"], c["layout"], reuse, src_rank))
+    ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
+    M = ctx.cfg.max_tokens
+    ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"],
+                          max_tokens=M if ll else 0, src_rank=src_rank, with_send=not ll)
+    x = to_dev_bf16(x_bits) if T else torch.empty((0, c["H"]), dtype=torch.bfloat16, device=dev())
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx)).to(dev())
+    w_d = torch.from_numpy(np.ascontiguousarray(w)).to(dev())
+    bufs = gpu.DispatchBuffers(ctx)
+    poison(bufs)
+    h = gpu.Handle(ctx)
+    h.pos.fill_(-7)
+
+    # ---- layout
+    cnt_e, cnt_r, in_rank = gpu.moe_dispatch_layout(ctx, idx_d)
+    # ---- dispatch
+    gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=reuse, bufs=bufs, handle=h)
+    st, flags = gpu.moe_poll_error(ctx)
+    assert st == (gpu.MOE_ERR_BAD_TOPK if ref["bad_ids"] else gpu.MOE_OK), (st, flags)
+
+    assert np.array_equal(bits_of(cnt_e), ref["num_tokens_per_expert"]), "num_tokens_per_expert"
+    assert np.array_equal(bits_of(cnt_r), ref["num_tokens_per_rank"]), "num_tokens_per_rank"
+    assert np.array_equal(bits_of(in_rank), ref["is_token_in_rank"]), "is_token_in_rank"
+    n_send, n_pairs = ref["n_send"], ref["n_pairs"]
+    assert np.array_equal(bits_of(h.expert_offsets), ref["expert_offsets"]), "expert_offsets"
+    assert np.array_equal(bits_of(h.rank_offsets), ref["rank_offsets"]), "rank_offsets"
+    assert np.array_equal(bits_of(h.recv_counts), ref["num_tokens_per_expert"]), "recv_counts"
+    pos_ref = ref["pos_ll"] if ll else ref["pos"]
+    assert np.array_equal(bits_of(h.pos[:T]), pos_ref), "handle pos"
+    assert np.array_equal(bits_of(h.recv_src_idx[:n_pairs]), ref["recv_src_idx"]), "recv_src_idx"
+    if not ll:
+        assert np.array_equal(bits_of(h.send_src_idx[:n_send]), ref["send_src_idx"]), "send_src_idx"
+
+    # ---- payload rows
+    valid = ref["pos"] >= 0
+    rowdt = np.uint8 if fp8 else np.uint16
+    if ll:
+        dst = torch.from_numpy(pos_ref[valid].astype(np.int64)).to(dev())
+        got = bits_of(bufs.recv_rows[dst]).view(rowdt)
+        assert np.array_equal(got, ref["recv_rows"][ref["pos"][valid]]), "LL receive rows"
+        if fp8:
+            assert np.array_equal(bits_of(bufs.recv_scales[dst]), ref["recv_scales"][ref["pos"][valid]])
+        if check_poison:
+            # exactly the routed slots were written
+            r8 = bufs.recv_rows.view(torch.uint8)
+            rows = r8.view(c["E"], -1, r8.shape[1])
+            written = 0
+            for e0 in range(0, c["E"], 16):
+                blk = rows[e0:e0 + 16]
+                written += int((blk[:, :, :64] != POISON).any(dim=2).sum())
+            assert written == n_pairs, ("LL slots written", written, n_pairs)
+    else:
+        got = bits_of(bufs.recv_rows[:n_pairs]).view(rowdt)
+        assert np.array_equal(got, ref["recv_rows"]), "expert-major receive rows"
+        got = bits_of(bufs.send_rows[:n_send]).view(rowdt)
+        assert np.array_equal(got, ref["send_rows"]), "send rows"
+        if fp8:
+            assert np.array_equal(bits_of(bufs.recv_scales[:n_pairs]), ref["recv_scales"])
+            assert np.array_equal(bits_of(bufs.send_scales[:n_send]), ref["send_scales"])
+        if check_poison:
+            for t, n in ((bufs.recv_rows, n_pairs), (bufs.send_rows, n_send),
+                         (bufs.recv_scales, n_pairs), (bufs.send_scales, n_send)):
+                if t is not None and n < t.shape[0]:
+                    assert bool((t[n:].view(torch.uint8) == POISON).all()), "stray write past the valid rows"
+
+    # ---- combine: N(0,1) expert outputs at the routed rows, NaN elsewhere
+    n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
+    y = torch.empty((n_cap, c["H"]), dtype=torch.bfloat16, device=dev())
+    y.view(torch.int16).fill_(0x7FC0)
+    yv = W.expert_outputs({"cfg": c}, n_pairs)
+    if n_pairs:
+        if ll:
+            y[dst] = to_dev_bf16(yv[ref["pos"][valid]])
+        else:
+            y[:n_pairs] = to_dev_bf16(yv)
+    out = gpu.moe_combine(ctx, y, w_d, h)
+    st, flags = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK, (st, flags)
+    out_ref = oracle.combine(yv, w, ref["pos"])
+    got = bits_of(out)
+    d = np.abs(pins.bf16_ordered(got) - pins.bf16_ordered(out_ref))
+    n_diff = int((d != 0).sum())
+    log("  combine: %d of %d elements differ from the oracle, max %d ulp" % (n_diff, d.size, d.max(initial=0)))
+    assert d.max(initial=0) <= 1, "combine beyond 1 bf16 ulp"
+    assert n_diff == 0, "combine expected bit-exact (separately rounded fp32 multiply and add)"
+    del y
+    ctx.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return ref
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "grouped", "skewed"])
+def test_workload_full_size(gpu, name):
+    d = W.make(name)
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], reuse=True, tag=name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "grouped"])
+def test_workload_without_layout_reuse(gpu, name):
+    d = W.make(name, T=min(W.WORKLOADS[name]["T"], 1024))
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], reuse=False, tag=name)
+
+
+# ---------------------------------------------------------------- ragged / edge cases
+def small_cfg(name, H=512):
+    c = dict(W.WORKLOADS[name])
+    c["H"] = H
+    return c
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 255, 256, 257, 1000])
+@pytest.mark.parametrize("name", ["prefill", "grouped", "decode"])
+def test_ragged_token_counts(gpu, name, T):
+    c = small_cfg(name)
+    d = W.make(name, T=T)
+    x = d["x"][:, :c["H"]].copy()
+    M = max(T, 1) + 37 if c["layout"] == W.LAYOUT_CONTIGUOUS else max(T, 1)
+    c["max_tokens"] = M
+    run_case(gpu, c, x, d["topk_idx"], d["topk_weights"], max_tokens=M, tag="ragged-%s" % name)
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_empty_slots(gpu, name):
+    c = small_cfg(name)
+    d = W.make(name, T=300)
+    idx = W.with_empty_slots(d["topk_idx"], 0.3)
+    idx[5, :] = -1                       # a token with no expert at all
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), idx, d["topk_weights"], max_tokens=300, tag="empty-slots")
+
+
+def test_all_tokens_one_expert(gpu):
+    c = small_cfg("skewed", H=256)
+    T = 2000
+    d = W.make("skewed", T=T)
+    idx = np.full((T, c["k"]), -1, np.int64)
+    idx[:, 0] = 7                        # every token to expert 7 (one huge segment)
+    idx[::3, 1] = 63
+    run_case(gpu, c, d["x"][:, :256].copy(), idx, d["topk_weights"], max_tokens=T, tag="one-expert")
+
+
+def test_duplicate_experts_in_a_row(gpu):
+    c = small_cfg("prefill", H=256)
+    T = 700
+    rng = np.random.Generator(np.random.PCG64(9))
+    idx = rng.integers(0, 4, (T, c["k"])).astype(np.int64)    # many repeats within rows
+    d = W.make("prefill", T=T)
+    run_case(gpu, c, d["x"][:, :256].copy(), idx, d["topk_weights"], max_tokens=T, tag="duplicates")
+
+
+def test_bad_expert_ids(gpu):
+    c = small_cfg("grouped", H=256)
+    T = 400
+    d = W.make("grouped", T=T)
+    idx = d["topk_idx"].copy()
+    idx[3, 2] = c["E"]            # out of range -> error flag, slot treated as empty
+    idx[10, 0] = -5
+    idx[399, 7] = 1 << 40
+    run_case(gpu, c, d["x"][:, :256].copy(), idx, d["topk_weights"], max_tokens=T, tag="bad-ids")
+
+
+def test_low_latency_other_source_rank(gpu):
+    c = small_cfg("decode")
+    d = W.make("decode", T=100)
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), d["topk_idx"], d["topk_weights"], max_tokens=128,
+             src_rank=c["R"] - 3, tag="ll-s0")
+
+
+def test_limits(gpu):
+    """Largest supported expert count, rank count and top-k at once."""
+    c = dict(index=9, T=3000, H=128, E=1024, R=64, k=32, quant=W.QUANT_FP8,
+             layout=W.LAYOUT_CONTIGUOUS, max_tokens=3000)
+    rng = np.random.Generator(np.random.PCG64(4))
+    idx = W.route_uniform(rng, c["T"], c["E"], c["k"])
+    x = W.to_bf16_bits(rng.standard_normal((c["T"], c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, c["T"], c["k"])
+    run_case(gpu, c, x, idx, w, max_tokens=c["T"], tag="limits")
+
+
+# ---------------------------------------------------------------- fp8 codec
+def test_fp8_codec_exhaustive_bf16(gpu):
+    """Blocks whose max is 448 quantise with scale exactly 1, so the GPU's
+    E4M3 conversion is compared on every finite bf16 value of magnitude <= 448
+    (ties, subnormal codes, signed zeros) -- and on a second scale (block max
+    3.0, scale 448/3) that exercises full binary32 products."""
+    v = pins.all_bf16_finite_f32()
+    v = v[np.abs(v) <= 448]
+    for amax in (448.0, 3.0):
+        vv = v[np.abs(v) <= amax]
+        per_row = 127 * 8               # 8 blocks of 128 (one slot per block holds amax)
+        n = -(-vv.size // per_row)
+        flat = np.zeros(n * per_row, np.float32)
+        flat[:vv.size] = vv
+        blocks = np.zeros((n * 8, 128), np.float32)
+        blocks[:, :127] = flat.reshape(n * 8, 127)
+        blocks[:, 127] = amax
+        x = W.to_bf16_bits(blocks.reshape(n, 1024))
+        c = dict(index=8, T=n, H=1024, E=8, R=2, k=1, quant=W.QUANT_FP8,
+                 layout=W.LAYOUT_CONTIGUOUS, max_tokens=n)
+        idx = np.zeros((n, 1), np.int64)
+        idx[:, 0] = np.arange(n) % 8
+        w = np.ones((n, 1), np.float32)
+        ref = run_case(gpu, c, x, idx, w, max_tokens=n, tag="codec-amax%g" % amax)
+        if amax == 448.0:
+            q, _ = oracle.quant_rows(x)
+            assert np.array_equal(q.reshape(-1, 128)[:, :127].ravel()[:vv.size], pins.brute_e4m3_encode(vv))
+        del ref
+
+
+# ---------------------------------------------------------------- round trip
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_identity_expert_roundtrip(gpu, name):
+    """Dispatch, identity expert (y = received rows), combine with weights
+    summing to one: the output is x (the method's defining invariant)."""
+    d = W.make(name, T=1024)
+    c = d["cfg"]
+    ctx = make_ctx(gpu, c, 1024)
+    x = to_dev_bf16(d["x"])
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    bufs, h = gpu.moe_dispatch(ctx, x, idx)
+    out = gpu.moe_combine(ctx, bufs.recv_rows, w, h)
+    xb = d["x"].copy()
+    xb[xb == 0x8000] = 0
+    assert np.array_equal(bits_of(out), xb)
+    ctx.close()
+
+
+# ---------------------------------------------------------------- API errors
+def test_api_errors(gpu):
+    c = small_cfg("prefill", H=256)
+    d = W.make("prefill", T=64)
+    ctx = make_ctx(gpu, c, 64, max_tokens=64)
+    x = to_dev_bf16(d["x"][:, :256].copy())
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    # reuse without a matching layout
+    with pytest.raises(gpu.MoeError) as e:
+        gpu.moe_dispatch(ctx, x, idx, reuse_layout=True)
+    assert e.value.status == gpu.MOE_ERR_INVALID_ARG
+    gpu.moe_dispatch_layout(ctx, idx)
+    with pytest.raises(gpu.MoeError):
+        gpu.moe_dispatch(ctx, x, idx.clone(), reuse_layout=True)   # another topk_idx buffer
+    # capacity
+    big = W.make("prefill", T=65)
+    with pytest.raises(gpu.MoeError) as e:
+        gpu.moe_dispatch(ctx, to_dev_bf16(big["x"][:, :256].copy()),
+                         torch.from_numpy(big["topk_idx"]).to(dev()))
+    assert e.value.status == gpu.MOE_ERR_CAPACITY
+    # handle from another configuration is refused before anything is launched
+    bufs, h = gpu.moe_dispatch(ctx, x, idx)
+    c2 = dict(c)
+    c2["k"] = 4
+    ctx2 = make_ctx(gpu, c2, 64, max_tokens=64)
+    y = torch.zeros((64 * 8, 256), dtype=torch.bfloat16, device=dev())
+    lib = gpu.load_library()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    assert lib.moe_combine(ctx2.handle, p(y), p(w), ctypes.byref(h.c), p(y), None) == gpu.MOE_ERR_HANDLE
+    bad = gpu._binding.moe_handle.from_buffer_copy(h.c)
+    bad.num_tokens = 65
+    assert lib.moe_combine(ctx.handle, p(y), p(w), ctypes.byref(bad), p(y), None) == gpu.MOE_ERR_HANDLE
+    st, _ = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK
+    ctx.close()
+    ctx2.close()
+
+
+def test_timing_api(gpu):
+    d = W.make("tiny")
+    c = d["cfg"]
+    ctx = make_ctx(gpu, c, 16)
+    x = to_dev_bf16(d["x"])
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    ctx.timing_begin(16)
+    for _ in range(3):
+        gpu.moe_dispatch_layout(ctx, idx)
+        gpu.moe_dispatch(ctx, x, idx, reuse_layout=True)
+    r = ctx.timing_end()
+    assert r["layout"]["launches"] == 3 and r["dispatch"]["launches"] == 3
+    assert r["combine"]["launches"] == 0
+    assert r["dispatch"]["total_ms"] > 0
+    ctx.close()
+
+
+def test_native_library_is_in_tree(gpu):
+    import os
+    lib = gpu.load_library()
+    assert os.path.dirname(os.path.abspath(lib._name)) == os.path.dirname(os.path.abspath(gpu.LIB_PATH))
