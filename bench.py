@@ -1,0 +1,259 @@
+"""Benchmark: MoE dispatch layout + dispatch + combine on one MI355X.
+
+One step = the whole hot path over one batch: moe_dispatch_layout, then
+moe_dispatch reusing that layout, then moe_combine of the expert outputs.
+Default workload: prefill, 4096 tokens x hidden 7168, 256 experts over 32
+virtual ranks, top-8, bf16 dispatch into per-rank send buffers and the
+expert-major receive layout, bf16 combine.  Inputs are resident in HBM before
+the timed region; nothing is allocated inside it.
+
+value = algorithmic HBM bytes of one step (x read once, every destination row
+written once, expert outputs read once, outputs written once, routing
+metadata) / measured time per step, in GB/s.  The per-kernel roofline uses
+durations measured with HIP events the library records on its own launch
+stream around each kernel (moe_timing_begin / moe_timing_end).
+
+Prints ONE JSON line.  --gpus N with N > 1 is refused: this build drives one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor spec
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="prefill",
+                   choices=["tiny", "decode", "prefill", "grouped", "skewed"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true", help="skip the 128-token decode side measurement")
+    p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--profile-only", action="store_true",
+                   help="run warmup + steps only (for rocprofv3), print the JSON line without baselines")
+    return p.parse_args()
+
+
+def algorithmic_bytes(c, T, n_send, n_pairs, n_slots):
+    """Bytes the method must move per launch of each kernel (actual counts)."""
+    H, k, E, R = c["H"], c["k"], c["E"], c["R"]
+    fp8 = c["quant"] == 1
+    B = (H + 4 * (H // 128)) if fp8 else 2 * H          # payload bytes per dispatched row
+    ll = c["layout"] == 1
+    layout = 8 * T * k + 4 * E + 4 * R + T * R
+    if ll:
+        dispatch = 2 * T * H + 8 * T * k + B * n_pairs + 8 * n_pairs + 4 * (2 * E + R + 2)
+    else:
+        dispatch = (2 * T * H + 8 * T * k + B * (n_send + n_pairs) + 4 * n_send + 8 * n_pairs
+                    + 4 * (2 * E + R + 2))
+    combine = 2 * n_pairs * H + 8 * n_slots + 2 * T * H
+    return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def setup(moe, W, torch, name, T=None):
+    d = W.make(name, T=T)
+    c = d["cfg"]
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    cfg = moe.make_config(c["max_tokens"], c["H"], c["E"], c["R"], c["k"], 0, c["quant"], c["layout"])
+    ctx = moe.Context(cfg)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    bufs = moe.DispatchBuffers(ctx)
+    h = moe.Handle(ctx)
+    cnt_e = torch.empty(c["E"], dtype=torch.int32, device=dev)
+    cnt_r = torch.empty(c["R"], dtype=torch.int32, device=dev)
+    in_rank = torch.empty((c["T"], c["R"]), dtype=torch.uint8, device=dev)
+    out = torch.empty((c["T"], c["H"]), dtype=torch.bfloat16, device=dev)
+    # expert outputs: N(0,1) bf16 in the receive layout, drawn on the GPU (seeded)
+    n_rows = ctx.hint(moe.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
+    y = torch.empty((n_rows, c["H"]), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(W.SEED_BASE + c["index"])
+    if c["layout"] == 0:
+        y.copy_(torch.randn((n_rows, c["H"]), generator=g, device=dev, dtype=torch.float32))
+    # first pass to learn the routing counts (and fill low-latency slots of y)
+    moe.moe_dispatch_layout(ctx, idx, cnt_e, cnt_r, in_rank)
+    moe.moe_dispatch(ctx, x, idx, reuse_layout=True, bufs=bufs, handle=h)
+    torch.cuda.synchronize()
+    n_pairs = int(h.expert_offsets[-1].item())
+    n_send = int(h.rank_offsets[-1].item())
+    if c["layout"] == 1:
+        pos = h.pos[:c["T"]].flatten()
+        pos = pos[pos >= 0].long()
+        y[pos] = torch.randn((pos.numel(), c["H"]), generator=g, device=dev,
+                             dtype=torch.float32).to(torch.bfloat16)
+    st, _ = moe.moe_poll_error(ctx)
+    assert st == moe.MOE_OK, st
+    return {"d": d, "c": c, "ctx": ctx, "x": x, "idx": idx, "w": w, "bufs": bufs, "h": h,
+            "cnt_e": cnt_e, "cnt_r": cnt_r, "in_rank": in_rank, "out": out, "y": y,
+            "n_pairs": n_pairs, "n_send": n_send}
+
+
+def step(moe, s):
+    moe.moe_dispatch_layout(s["ctx"], s["idx"], s["cnt_e"], s["cnt_r"], s["in_rank"])
+    moe.moe_dispatch(s["ctx"], s["x"], s["idx"], reuse_layout=True, bufs=s["bufs"], handle=s["h"])
+    moe.moe_combine(s["ctx"], s["y"], s["w"], s["h"], out=s["out"])
+
+
+def timed(moe, torch, s, steps, warmup):
+    """Wall-clock time of `steps` back-to-back steps, nothing else on the stream."""
+    for _ in range(warmup):
+        step(moe, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(moe, s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st, _ = moe.moe_poll_error(s["ctx"])
+    assert st == moe.MOE_OK, st
+    return wall
+
+
+def timed_kernels(moe, torch, s, steps, flush=None):
+    """Per-kernel durations from the HIP events the library records around
+    each of its launches, on its launch stream, over `steps` more steps.  The
+    events add a few microseconds per launch, so this pass is kept apart from
+    the wall-clock pass above.  With `flush`, a 1 GiB buffer is rewritten
+    between steps (outside the kernel events) so caches start cold."""
+    s["ctx"].timing_begin(3 * steps + 3)
+    for _ in range(steps):
+        if flush is not None:
+            flush.add_(1)
+        step(moe, s)
+    torch.cuda.synchronize()
+    kt = s["ctx"].timing_end()
+    st, _ = moe.moe_poll_error(s["ctx"])
+    assert st == moe.MOE_OK, st
+    return kt
+
+
+def cpu_baseline(s, reps):
+    """The oracle as it stands (single-threaded scalar C) on the same inputs."""
+    import numpy as np
+    import oracle
+    d, c = s["d"], s["c"]
+    y = s["y"][:s["n_pairs"]].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
+        oracle.combine(y, d["topk_weights"], r["pos"])
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), r
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py drives a single GPU: this build has no multi-GPU path "
+              "(peer transport is replaced by a local copy); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import combine_moe_dispatch_layout_amd as moe
+    import workloads as W
+    moe.load_library()
+    torch.cuda.set_device(0)
+
+    s = setup(moe, W, torch, a.workload)
+    c = s["c"]
+    T = c["T"]
+    alg = algorithmic_bytes(c, T, s["n_send"], s["n_pairs"], T * c["k"])
+    step_bytes = sum(alg.values())
+    wall = timed(moe, torch, s, a.steps, a.warmup)
+    kt = timed_kernels(moe, torch, s, a.steps)
+    ms_per_step = 1e3 * wall / a.steps
+    value = step_bytes / (wall / a.steps) / 1e9
+
+    per_kernel = {}
+    for name in ("layout", "dispatch", "combine"):
+        n = kt[name]["launches"]
+        us = 1e3 * kt[name]["total_ms"] / n
+        per_kernel[name] = {"us": round(us, 2), "alg_bytes": alg[name],
+                            "GB/s": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+    dom = max(("layout", "dispatch", "combine"), key=lambda n: per_kernel[n]["us"])
+    achieved = per_kernel[dom]["GB/s"]
+
+    line = {
+        "metric": "dispatch+combine us/call and HBM GB/s (% of peak), 128 & 4096 tok x 7168, top-8",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3/bf16" if c["quant"] else "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and expert outputs, routing per workload)",
+        "config": {"workload": "%s: T=%d H=%d E=%d R=%d top-%d %s %s" % (
+            a.workload, T, c["H"], c["E"], c["R"], c["k"], "fp8" if c["quant"] else "bf16",
+            "padded-LL" if c["layout"] else "send+contiguous"),
+            "step": "layout + dispatch(reuse layout) + combine",
+            "alg_bytes_per_step": step_bytes, "n_send_rows": s["n_send"], "n_recv_rows": s["n_pairs"],
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
+        "kernels": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(dom, a.workload)},
+    }
+
+    if not a.profile_only and not a.no_decode and a.workload != "decode":
+        sd = setup(moe, W, torch, "decode")
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > 256 MB MALL
+        wall_d = timed(moe, torch, sd, 500, 50)
+        kt_d = timed_kernels(moe, torch, sd, 100, flush=flush)
+        alg_d = algorithmic_bytes(sd["c"], 128, 0, sd["n_pairs"], 128 * 8)
+        warm_us = 1e6 * wall_d / 500
+        cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("layout", "dispatch", "combine")}
+        line["decode"] = {
+            "workload": "decode: T=128 H=7168 E=256 R=32 top-8 fp8 padded-LL",
+            "us_per_step_warm": round(warm_us, 2),
+            "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
+            "us_per_step_cold": round(sum(cold.values()), 2),
+            "GB/s_warm": round(sum(alg_d.values()) / (warm_us * 1e-6) / 1e9, 1)}
+        sd["ctx"].close()
+        del sd, flush
+        torch.cuda.empty_cache()
+
+    if not a.profile_only and not a.no_cpu_baseline:
+        sec, _ = cpu_baseline(s, a.cpu_reps)
+        line["cpu_baseline"] = {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": "the full %s workload (%d tokens): layout, positions, payload "
+                                          "rows and combine in the scalar C oracle, median of %d runs, "
+                                          "%.2f s each" % (a.workload, T, a.cpu_reps, sec)}
+    print(json.dumps(line), flush=True)
+    s["ctx"].close()
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, only while the kernel source is unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", "moe_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    ent = rec.get(workload, {}).get(kernel)
+    if ent is None or ent.get("kernel_source_sha256") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+if __name__ == "__main__":
+    main()

@@ -19,10 +19,12 @@ constexpr uint32_t kErrBounds = 2u;
 struct LayoutArgs {
     const int64_t* topk_idx;   // [T, k]
     int32_t T, k, E, R, El;
-    int32_t ebits, rbits;      // bits needed to hold an expert id / a rank id
+    uint32_t k_magic;          // ceil(2^20 / k):  entry -> token division
+    uint32_t el_magic;         // ceil(2^20 / El): expert -> rank division
     int32_t max_tokens;        // row stride of srank
-    int32_t* tile_e;           // [ntiles, E]  per-tile counts -> global row bases
-    int32_t* tile_r;           // [ntiles, R]
+    int32_t* tile_cnt;         // [E + R, tile_stride]  per-tile counts, transposed
+    int32_t tile_stride;       // >= number of tiles, multiple of 4
+    int32_t* grand_tot;        // [E + R]  totals over tiles (atomics; zero between launches)
     uint16_t* erank;           // [T, k]       rank of slot (t, j) among its expert's rows in the tile
     uint16_t* srank;           // [R, max_tokens] rank of token t among the tile's tokens sent to r
     int32_t* cnt_e;            // [E]   workspace copies of the results
@@ -45,8 +47,8 @@ struct PackArgs {
     int32_t max_tokens;
     int32_t s0;
     int64_t cap;               // low-latency slots per expert (M * R)
-    const int32_t* tile_e;
-    const int32_t* tile_r;
+    const int32_t* tile_cnt;   // [E + R, tile_stride] per-tile counts, transposed
+    int32_t tile_stride;
     const uint16_t* erank;
     const uint16_t* srank;
     const int32_t* cnt_e;

@@ -26,7 +26,7 @@ namespace {
 constexpr uint32_t kTagMagic = 0x4d6f4500u;   // "MoE\0"
 
 struct Geometry {
-    int El, ksend, ntiles_max, ebits, rbits;
+    int El, ksend, ntiles_max, rbits;
     int64_t cap, row_bytes, nb;
     int64_t send_rows, recv_rows;
 };
@@ -53,7 +53,6 @@ moe_status check_config(const moe_config* c, Geometry* g) {
     q.El = c->num_experts / c->num_ranks;
     q.ksend = std::min(c->topk, c->num_ranks);
     q.ntiles_max = (c->max_tokens + kTileTokens - 1) / kTileTokens;
-    q.ebits = bits_for(c->num_experts);
     q.rbits = bits_for(c->num_ranks);
     q.cap = (int64_t)c->max_tokens * c->num_ranks;
     q.row_bytes = c->quant == MOE_QUANT_FP8_E4M3 ? c->hidden : 2 * (int64_t)c->hidden;
@@ -71,11 +70,13 @@ moe_status check_config(const moe_config* c, Geometry* g) {
 
 // Workspace layout (device, one allocation, 256-byte aligned pieces).
 struct Workspace {
-    size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_e, off_tile_r,
+    size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
         off_erank, off_srank, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int tile_stride(const Geometry& g) { return (g.ntiles_max + 3) & ~3; }
 
 Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     Workspace w;
@@ -87,8 +88,8 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     w.off_cnt_r = take(4 * (size_t)c->num_ranks);
     w.off_eoff = take(4 * ((size_t)c->num_experts + 1));
     w.off_roff = take(4 * ((size_t)c->num_ranks + 1));
-    w.off_tile_e = take(4 * (size_t)g.ntiles_max * c->num_experts);
-    w.off_tile_r = take(4 * (size_t)g.ntiles_max * c->num_ranks);
+    w.off_tile_cnt = take(4 * (size_t)tile_stride(g) * (c->num_experts + c->num_ranks));
+    w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
     w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
     w.total = o;
@@ -106,26 +107,20 @@ uint32_t config_tag(const moe_config* c) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest power-of-two chunk count per lane not above `need` (1..16).
-int pow2_floor16(int64_t need) {
-    int c = 1;
-    while (c < 16 && (int64_t)c * 2 <= need) c *= 2;
-    return c;
-}
-
 // Work split of a row-streaming kernel: each wavefront handles `chunks`
-// 16-byte chunks per lane of one token row (a "slice").  Whole rows per
-// wavefront when there are enough tokens to fill the chip; otherwise rows are
-// cut into more slices so that at least ~8 wavefronts per CU are in flight.
-void row_split(int64_t T, int64_t nchunk, int forced, int* chunks, int* nslices) {
+// 16-byte chunks per lane of one token row (a "slice"), at most `cap`.  Rows
+// are cut into more slices when there are too few tokens to keep ~8
+// wavefronts per CU in flight.  Measured on MI355X: dispatch is fastest with
+// whole rows per wavefront (cap 16), combine with short slices (cap 2).
+void row_split(int64_t T, int64_t nchunk, int forced, int cap, int* chunks, int* nslices) {
     int c;
     if (forced > 0) {
         c = forced;
     } else {
         const int64_t per_lane = (nchunk + 63) / 64;
         c = 1;
-        while (c < 16 && c < per_lane) c *= 2;                   // ceil to pow2, whole row
-        const int64_t target_items = 256 * 8;                    // 8 wavefronts per CU
+        while (c < cap && c < per_lane) c *= 2;
+        const int64_t target_items = 256 * 8;
         while (c > 1 && T * ((nchunk + 64 * c - 1) / (64 * c)) < target_items) c /= 2;
     }
     *chunks = c;
@@ -193,11 +188,12 @@ moe_status run_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t T, int32_t*
     a.E = c.num_experts;
     a.R = c.num_ranks;
     a.El = ctx->g.El;
-    a.ebits = ctx->g.ebits;
-    a.rbits = ctx->g.rbits;
+    a.k_magic = (uint32_t)(((1u << 20) + c.topk - 1) / c.topk);
+    a.el_magic = (uint32_t)(((1u << 20) + ctx->g.El - 1) / ctx->g.El);
     a.max_tokens = c.max_tokens;
-    a.tile_e = ctx->i32(ctx->wl.off_tile_e);
-    a.tile_r = ctx->i32(ctx->wl.off_tile_r);
+    a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
+    a.tile_stride = tile_stride(ctx->g);
+    a.grand_tot = ctx->i32(ctx->wl.off_grand_tot);
     a.erank = ctx->u16(ctx->wl.off_erank);
     a.srank = ctx->u16(ctx->wl.off_srank);
     a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
@@ -299,8 +295,8 @@ MOE_API moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out) {
         delete ctx;
         return MOE_ERR_HIP;
     }
-    // error word and arrival counter start at zero; the rest is written before it is read
-    if (hipMemset(ctx->ws, 0, 256 * 2) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    // error word, arrival counter and grand totals start at zero
+    if (hipMemset(ctx->ws, 0, ctx->wl.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(ctx->ws);
         delete ctx;
         return MOE_ERR_HIP;
@@ -392,8 +388,8 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     a.max_tokens = c.max_tokens;
     a.s0 = c.src_rank;
     a.cap = ctx->g.cap;
-    a.tile_e = ctx->i32(ctx->wl.off_tile_e);
-    a.tile_r = ctx->i32(ctx->wl.off_tile_r);
+    a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
+    a.tile_stride = tile_stride(ctx->g);
     a.erank = ctx->u16(ctx->wl.off_erank);
     a.srank = ctx->u16(ctx->wl.off_srank);
     a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
@@ -414,7 +410,7 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     a.h_recv_counts = handle->recv_counts;
     a.err = ctx->err();
     int chunks, nslices;
-    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, &chunks, &nslices);
+    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, 16, &chunks, &nslices);
     a.nslices = nslices;
     // at least one block so that the handle's offsets and counts are written for T = 0
     PackArgs a0 = a;
@@ -457,7 +453,7 @@ MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float
     a.rows_cap = ctx->g.recv_rows;
     a.err = ctx->err();
     int chunks, nslices;
-    row_split(T, c.hidden / 8, ctx->combine_chunks, &chunks, &nslices);
+    row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE);

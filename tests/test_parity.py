@@ -351,3 +351,16 @@ def test_native_library_is_in_tree(gpu):
     import os
     lib = gpu.load_library()
     assert os.path.dirname(os.path.abspath(lib._name)) == os.path.dirname(os.path.abspath(gpu.LIB_PATH))
+
+
+@pytest.mark.parametrize("E,R,k", [(1024, 1, 8), (64, 64, 8), (96, 3, 5), (1024, 64, 17)])
+def test_expert_rank_extremes(gpu, E, R, k):
+    """One rank holding every expert, one expert per rank, and odd sizes."""
+    T = 777
+    c = dict(index=10, T=T, H=128, E=E, R=R, k=k, quant=W.QUANT_BF16,
+             layout=W.LAYOUT_CONTIGUOUS, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(E + R + k))
+    idx = W.route_uniform(rng, T, E, k)
+    x = W.to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32))
+    w = W.softmax_weights(rng, T, k)
+    run_case(gpu, c, x, idx, w, max_tokens=T, tag="extremes")
