@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-reps", type=int, default=3)
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + steps only (for rocprofv3), print the JSON line without baselines")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run five 1 GiB device-to-device copies (known bytes) so that rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE counters can be scaled")
     return p.parse_args()
 
 
@@ -161,6 +164,17 @@ def main():
               "(peer transport is replaced by a local copy); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.copy_calibration:
+        torch.cuda.set_device(0)
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
+                          "copies": 5}), flush=True)
+        return
     import combine_moe_dispatch_layout_amd as moe
     import workloads as W
     moe.load_library()
