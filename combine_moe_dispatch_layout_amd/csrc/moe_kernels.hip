@@ -104,7 +104,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
 // returns the total; all threads of the block must call it.  `wsum` is
 // kWavesPerBlock ints of LDS scratch.
 __device__ __forceinline__ int block_exclusive_scan(const int32_t* v, int32_t* out, int n, int32_t* wsum) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int per = (n + kBlockThreads - 1) / kBlockThreads;
     const int lo = tid * per < n ? tid * per : n;
     const int hi = lo + per < n ? lo + per : n;
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     __shared__ int32_t wsum[kWavesPerBlock];
     __shared__ int s_last;
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int E = a.E, R = a.R, k = a.k;
     const int ntiles = gridDim.x;
     for (int i = tid; i < kWavesPerBlock * E; i += kBlockThreads) {
@@ -296,10 +298,44 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     }
 }
 
+// Chunk i of a wavefront's slice starts at 16-byte chunk gi = gbase + 64 i.
+// Whole iterations (gi + 64 <= nchunk) need no per-lane guard: the test is
+// wave-uniform, so the stores are issued unmasked; only a ragged last
+// iteration masks lanes.
+enum ChunkState { kChunkFull, kChunkPart, kChunkNone };
+__device__ __forceinline__ ChunkState chunk_state(int64_t gi, int64_t nchunk) {
+    return gi + 64 <= nchunk ? kChunkFull : (gi < nchunk ? kChunkPart : kChunkNone);
+}
+
 // ============================================================== dispatch
+// Store a slice (C chunks per lane) of one row.
+template <int C, typename V>
+__device__ __forceinline__ void store_row(V* dst, const V* v, int64_t gbase, int lane, int64_t nchunk) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int64_t gi = gbase + i * 64;
+        const ChunkState cs = chunk_state(gi, nchunk);
+        if (cs == kChunkFull) dst[gi + lane] = v[i];
+        else if (cs == kChunkPart && gi + lane < nchunk) dst[gi + lane] = v[i];
+    }
+}
+
+// Per-block scales of a slice: the first lane of each 16-lane block group.
+template <int C>
+__device__ __forceinline__ void store_scales(float* sdst, const float* sinv, int64_t g0, int lane, int64_t nchunk) {
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t g = g0 + i * 64;
+            if (g < nchunk) sdst[g >> 4] = sinv[i];
+        }
+    }
+}
+
 template <int C, bool FP8, bool LL, bool SEND>
 __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     if (blockIdx.x == 0) {   // handle copies of the layout offsets and counts
         for (int i = tid; i <= a.E; i += kBlockThreads) a.h_eoff[i] = a.eoff[i];
         for (int i = tid; i < a.E; i += kBlockThreads) a.h_recv_counts[i] = a.cnt_e[i];
@@ -315,13 +351,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
     // ---- load this slice of the row once (issued before the routing lookups,
     // which it does not depend on)
     const int64_t nchunk = a.H / 8;                   // 16-byte bf16 chunks per row
-    const int64_t g0 = (int64_t)s * 64 * C + lane;
+    const int64_t gbase = (int64_t)s * 64 * C;        // first chunk of this slice
+    const int64_t g0 = gbase + lane;
     const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.H);
     u32x4 v[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int64_t g = g0 + i * 64;
-        v[i] = g < nchunk ? src[g] : u32x4{0u, 0u, 0u, 0u};
+        const ChunkState cs = chunk_state(gbase + i * 64, nchunk);
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) v[i] = src[g];
     }
 
     // ---- routing of token t: lane j < k owns slot j
@@ -371,24 +410,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
     if constexpr (!FP8) {
         for (int j = 0; j < k; ++j) {
             const int rr = readlane(rrow, j);
-            if (rr >= 0) {
-                u32x4* dst = reinterpret_cast<u32x4*>(a.recv_rows) + (int64_t)rr * nchunk;
-#pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    const int64_t g = g0 + i * 64;
-                    if (g < nchunk) dst[g] = v[i];
-                }
-            }
+            if (rr >= 0) store_row<C>(reinterpret_cast<u32x4*>(a.recv_rows) + (int64_t)rr * nchunk, v, gbase, lane, nchunk);
             if constexpr (SEND) {
                 const int sr = readlane(srow, j);
-                if (sr >= 0) {
-                    u32x4* dst = reinterpret_cast<u32x4*>(a.send_rows) + (int64_t)sr * nchunk;
-#pragma unroll
-                    for (int i = 0; i < C; ++i) {
-                        const int64_t g = g0 + i * 64;
-                        if (g < nchunk) dst[g] = v[i];
-                    }
-                }
+                if (sr >= 0) store_row<C>(reinterpret_cast<u32x4*>(a.send_rows) + (int64_t)sr * nchunk, v, gbase, lane, nchunk);
             }
         }
     } else {
@@ -420,30 +445,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
         for (int j = 0; j < k; ++j) {
             const int rr = readlane(rrow, j);
             if (rr >= 0) {
-                u32x2* dst = reinterpret_cast<u32x2*>(a.recv_rows) + (int64_t)rr * nchunk;
-                float* sdst = a.recv_scales + (int64_t)rr * nb;
-#pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    const int64_t g = g0 + i * 64;
-                    if (g < nchunk) {
-                        dst[g] = q[i];
-                        if ((lane & 15) == 0) sdst[g >> 4] = sinv[i];
-                    }
-                }
+                store_row<C>(reinterpret_cast<u32x2*>(a.recv_rows) + (int64_t)rr * nchunk, q, gbase, lane, nchunk);
+                store_scales<C>(a.recv_scales + (int64_t)rr * nb, sinv, g0, lane, nchunk);
             }
             if constexpr (SEND) {
                 const int sr = readlane(srow, j);
                 if (sr >= 0) {
-                    u32x2* dst = reinterpret_cast<u32x2*>(a.send_rows) + (int64_t)sr * nchunk;
-                    float* sdst = a.send_scales + (int64_t)sr * nb;
-#pragma unroll
-                    for (int i = 0; i < C; ++i) {
-                        const int64_t g = g0 + i * 64;
-                        if (g < nchunk) {
-                            dst[g] = q[i];
-                            if ((lane & 15) == 0) sdst[g >> 4] = sinv[i];
-                        }
-                    }
+                    store_row<C>(reinterpret_cast<u32x2*>(a.send_rows) + (int64_t)sr * nchunk, q, gbase, lane, nchunk);
+                    store_scales<C>(a.send_scales + (int64_t)sr * nb, sinv, g0, lane, nchunk);
                 }
             }
         }
@@ -453,7 +462,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
 // ============================================================== combine
 template <int C, int KMAX>
 __global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w;
     if (item >= (int64_t)a.T * a.nslices) return;
     const int t = (int)(item / a.nslices);
@@ -485,7 +495,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int64_t g = g0 + i * 64;
-        if (g < nchunk) {
+        const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
+        if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
             u32x4 v[KMAX];
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
