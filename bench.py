@@ -104,19 +104,27 @@ def setup(moe, W, torch, name, T=None):
 
 
 def step(moe, s):
+    """Layout, dispatch reusing that layout, combine (the normal-mode call sequence)."""
     moe.moe_dispatch_layout(s["ctx"], s["idx"], s["cnt_e"], s["cnt_r"], s["in_rank"])
     moe.moe_dispatch(s["ctx"], s["x"], s["idx"], reuse_layout=True, bufs=s["bufs"], handle=s["h"])
     moe.moe_combine(s["ctx"], s["y"], s["w"], s["h"], out=s["out"])
 
 
-def timed(moe, torch, s, steps, warmup):
+def step_ll(moe, s):
+    """Low-latency call sequence: dispatch straight from topk_idx (the routing is
+    computed inside the fused dispatch launch), then combine."""
+    moe.moe_dispatch(s["ctx"], s["x"], s["idx"], reuse_layout=False, bufs=s["bufs"], handle=s["h"])
+    moe.moe_combine(s["ctx"], s["y"], s["w"], s["h"], out=s["out"])
+
+
+def timed(moe, torch, s, steps, warmup, fn=step):
     """Wall-clock time of `steps` back-to-back steps, nothing else on the stream."""
     for _ in range(warmup):
-        step(moe, s)
+        fn(moe, s)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(moe, s)
+        fn(moe, s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st, _ = moe.moe_poll_error(s["ctx"])
@@ -124,7 +132,7 @@ def timed(moe, torch, s, steps, warmup):
     return wall
 
 
-def timed_kernels(moe, torch, s, steps, flush=None):
+def timed_kernels(moe, torch, s, steps, flush=None, fn=step):
     """Per-kernel durations from the HIP events the library records around
     each of its launches, on its launch stream, over `steps` more steps.  The
     events add a few microseconds per launch, so this pass is kept apart from
@@ -134,7 +142,7 @@ def timed_kernels(moe, torch, s, steps, flush=None):
     for _ in range(steps):
         if flush is not None:
             flush.add_(1)
-        step(moe, s)
+        fn(moe, s)
     torch.cuda.synchronize()
     kt = s["ctx"].timing_end()
     st, _ = moe.moe_poll_error(s["ctx"])
@@ -184,19 +192,24 @@ def main():
     c = s["c"]
     T = c["T"]
     alg = algorithmic_bytes(c, T, s["n_send"], s["n_pairs"], T * c["k"])
+    fn = step_ll if c["layout"] == 1 else step
+    if fn is step_ll:
+        alg["layout"] = 0                     # the routing is read inside the fused dispatch
     step_bytes = sum(alg.values())
-    wall = timed(moe, torch, s, a.steps, a.warmup)
-    kt = timed_kernels(moe, torch, s, a.steps)
+    wall = timed(moe, torch, s, a.steps, a.warmup, fn=fn)
+    kt = timed_kernels(moe, torch, s, a.steps, fn=fn)
     ms_per_step = 1e3 * wall / a.steps
     value = step_bytes / (wall / a.steps) / 1e9
 
     per_kernel = {}
     for name in ("layout", "dispatch", "combine"):
         n = kt[name]["launches"]
+        if n == 0:
+            continue
         us = 1e3 * kt[name]["total_ms"] / n
         per_kernel[name] = {"us": round(us, 2), "alg_bytes": alg[name],
                             "GB/s": round(alg[name] / (us * 1e-6) / 1e9, 1)}
-    dom = max(("layout", "dispatch", "combine"), key=lambda n: per_kernel[n]["us"])
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     achieved = per_kernel[dom]["GB/s"]
 
     line = {
@@ -215,7 +228,8 @@ def main():
         "config": {"workload": "%s: T=%d H=%d E=%d R=%d top-%d %s %s" % (
             a.workload, T, c["H"], c["E"], c["R"], c["k"], "fp8" if c["quant"] else "bf16",
             "padded-LL" if c["layout"] else "send+contiguous"),
-            "step": "layout + dispatch(reuse layout) + combine",
+            "step": "dispatch from topk_idx (fused) + combine" if fn is step_ll
+                    else "layout + dispatch(reuse layout) + combine",
             "alg_bytes_per_step": step_bytes, "n_send_rows": s["n_send"], "n_recv_rows": s["n_pairs"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
         "kernels": per_kernel,
@@ -227,17 +241,19 @@ def main():
     if not a.profile_only and not a.no_decode and a.workload != "decode":
         sd = setup(moe, W, torch, "decode")
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > 256 MB MALL
-        wall_d = timed(moe, torch, sd, 500, 50)
-        kt_d = timed_kernels(moe, torch, sd, 100, flush=flush)
+        wall_d = timed(moe, torch, sd, 500, 50, fn=step_ll)
+        kt_d = timed_kernels(moe, torch, sd, 100, flush=flush, fn=step_ll)
         alg_d = algorithmic_bytes(sd["c"], 128, 0, sd["n_pairs"], 128 * 8)
+        ll_bytes = alg_d["dispatch"] + alg_d["combine"]      # routing is read inside dispatch
         warm_us = 1e6 * wall_d / 500
-        cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("layout", "dispatch", "combine")}
+        cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("dispatch", "combine")}
         line["decode"] = {
             "workload": "decode: T=128 H=7168 E=256 R=32 top-8 fp8 padded-LL",
+            "step": "dispatch from topk_idx (one fused launch) + combine",
             "us_per_step_warm": round(warm_us, 2),
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
-            "us_per_step_cold": round(sum(cold.values()), 2),
-            "GB/s_warm": round(sum(alg_d.values()) / (warm_us * 1e-6) / 1e9, 1)}
+            "alg_bytes_per_step": ll_bytes,
+            "GB/s_warm": round(ll_bytes / (warm_us * 1e-6) / 1e9, 1)}
         sd["ctx"].close()
         del sd, flush
         torch.cuda.empty_cache()

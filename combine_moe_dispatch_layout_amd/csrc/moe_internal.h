@@ -12,6 +12,11 @@ constexpr int kTileTokens = 256;
 constexpr int kBlockThreads = 256;
 constexpr int kWavesPerBlock = kBlockThreads / 64;
 
+// The fused low-latency dispatch handles up to this many (token, slot) entries
+// and tokens.
+constexpr int kFusedMaxEntries = 2048;
+constexpr int kFusedMaxTokens = 512;
+
 // Bits of the sticky device error word.
 constexpr uint32_t kErrBadTopk = 1u;
 constexpr uint32_t kErrBounds = 2u;
@@ -86,5 +91,7 @@ hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s);
 // chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16)
 hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s);
+// Low-latency dispatch without a separate layout launch (T * k <= kFusedMaxEntries).
+hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t s);
 
 }  // namespace moe

@@ -332,6 +332,55 @@ __device__ __forceinline__ void store_scales(float* sdst, const float* sinv, int
     }
 }
 
+// Max over each 16-lane row of the wavefront with DPP lane permutations
+// (quad xor 1, quad xor 2, mirror within 8, mirror within 16); inputs are
+// non-negative, so every lane ends with its row's maximum.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+    const int x = __float_as_int(v);
+    int y;
+    switch (ctrl_sel) {
+        case 0: y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+        case 1: y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+        case 2: y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+        default: y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return __int_as_float(y);
+}
+__device__ __forceinline__ float row16_max(float m) {
+    m = fmaxf(m, dpp_f(m, 0));
+    m = fmaxf(m, dpp_f(m, 1));
+    m = fmaxf(m, dpp_f(m, 2));
+    m = fmaxf(m, dpp_f(m, 3));
+    return m;
+}
+
+// E4M3 quantisation of a slice held in registers (C 16-byte bf16 chunks per
+// lane): the 16 lanes holding one 128-channel block reduce |x| with a DPP
+// row max; scale 448/a' and stored dequant scale a'/448 are correctly
+// rounded binary32 divisions (a' = max(amax, 1e-4)); codes come from
+// v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, round to nearest even).
+template <int C>
+__device__ __forceinline__ void quantize_slice(const u32x4* v, u32x2* q, float* sinv) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                      bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        float m = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(f[u]));
+        m = row16_max(m);
+        const float ap = m > 1e-4f ? m : 1e-4f;
+        const float sc = 448.0f / ap;
+        sinv[i] = ap / 448.0f;
+        int lo = 0, hi = 0;
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[0], sc), __fmul_rn(f[1], sc), lo, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[2], sc), __fmul_rn(f[3], sc), lo, true);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[4], sc), __fmul_rn(f[5], sc), hi, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[6], sc), __fmul_rn(f[7], sc), hi, true);
+        q[i] = u32x2{(uint32_t)lo, (uint32_t)hi};
+    }
+}
+
 template <int C, bool FP8, bool LL, bool SEND>
 __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -420,27 +469,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
         // ---- E4M3 quantisation, once per token; 16 lanes hold one 128-channel block
         u32x2 q[C];
         float sinv[C];
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
-                          bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
-            float m = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(f[u]));
-            m = fmaxf(m, __shfl_xor(m, 8, 16));
-            m = fmaxf(m, __shfl_xor(m, 4, 16));
-            m = fmaxf(m, __shfl_xor(m, 2, 16));
-            m = fmaxf(m, __shfl_xor(m, 1, 16));
-            const float ap = m > 1e-4f ? m : 1e-4f;
-            const float sc = 448.0f / ap;     // correctly rounded binary32 divide
-            sinv[i] = ap / 448.0f;
-            int lo = 0, hi = 0;
-            lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[0], sc), __fmul_rn(f[1], sc), lo, false);
-            lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[2], sc), __fmul_rn(f[3], sc), lo, true);
-            hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[4], sc), __fmul_rn(f[5], sc), hi, false);
-            hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(f[6], sc), __fmul_rn(f[7], sc), hi, true);
-            q[i] = u32x2{(uint32_t)lo, (uint32_t)hi};
-        }
+        quantize_slice<C>(v, q, sinv);
         const int nb = a.H / 128;
         for (int j = 0; j < k; ++j) {
             const int rr = readlane(rrow, j);
@@ -454,6 +483,150 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
                     store_row<C>(reinterpret_cast<u32x2*>(a.send_rows) + (int64_t)sr * nchunk, q, gbase, lane, nchunk);
                     store_scales<C>(a.send_scales + (int64_t)sr * nb, sinv, g0, lane, nchunk);
                 }
+            }
+        }
+    }
+}
+
+// ============================================================== fused low-latency dispatch
+// In the padded low-latency layout a slot's row is e * cap + s0 * M + (its
+// rank among the rows of expert e), so no global scan stands between the
+// routing and the copy: one launch does both.  One block per token; its 4
+// wavefronts split the row into at most 4 slices.  The block builds two LDS
+// histograms of the T * k routing entries -- all of them, and those of
+// earlier tokens -- with atomic adds (integer counts: order-free): a slot's
+// rank is the earlier-token count of its expert plus the earlier slots of its
+// own token, and the exclusive scan of the full histogram gives its
+// expert-major position (for the handle).  Block 0 also publishes the
+// handle's counts and offsets.  For T * k <= kFusedMaxEntries and
+// T <= kFusedMaxTokens.
+template <int C, bool FP8>
+__global__ __launch_bounds__(kBlockThreads) void k_ll_dispatch(PackArgs a) {
+    __shared__ int32_t tot[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // histogram of all entries (+ ranks, block 0)
+    __shared__ int32_t hb[MOE_MAX_EXPERTS];                    // histogram of entries of earlier tokens
+    __shared__ int32_t off[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // exclusive scans of tot
+    __shared__ unsigned long long tok_mask[kFusedMaxTokens];    // ranks of each token (block 0)
+    __shared__ int32_t wsum[kWavesPerBlock];
+    constexpr int kPerThread = kFusedMaxEntries / kBlockThreads;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int k = a.k, E = a.E, R = a.R, T = a.T;
+    const int nent = T * k;
+    const uint64_t below = lanes_below(lane);
+    const int t = blockIdx.x;                 // this block's token
+    const bool has_token = t < T;
+    const int s = w;                          // this wavefront's row slice
+    const bool has_slice = has_token && s < a.nslices;
+    const int before = t * k;                 // entries of earlier tokens
+    const bool b0 = blockIdx.x == 0;
+
+    // ---- row slice and routing entries, all loads issued first
+    const int64_t nchunk = a.H / 8;
+    const int64_t gbase = (int64_t)s * 64 * C;
+    const int64_t g0 = gbase + lane;
+    u32x4 v[C];
+    if (has_slice) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.H);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t g = g0 + i * 64;
+            const ChunkState cs = chunk_state(gbase + i * 64, nchunk);
+            v[i] = u32x4{0u, 0u, 0u, 0u};
+            if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) v[i] = src[g];
+        }
+    }
+    int e = -1;
+    if (has_token && lane < k) {
+        const int64_t vv = a.topk_idx[(int64_t)before + lane];
+        if (vv >= 0 && vv < E) e = (int)vv;
+    }
+    int64_t ent[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = u * kBlockThreads + tid;
+        ent[u] = i < nent ? a.topk_idx[i] : -1;
+    }
+    for (int i = tid; i < E + R; i += kBlockThreads) tot[i] = 0;
+    for (int i = tid; i < E; i += kBlockThreads) hb[i] = 0;
+    if (b0) for (int i = tid; i < T; i += kBlockThreads) tok_mask[i] = 0ull;
+    __syncthreads();
+
+    // ---- histograms (integer counts: order-free)
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = u * kBlockThreads + tid;
+        const int64_t ee = ent[u];
+        if (ee >= 0 && ee < E) {
+            atomicAdd(&tot[(int)ee], 1);
+            if (i < before) atomicAdd(&hb[(int)ee], 1);
+            if (b0) atomicOr(&tok_mask[i / k], 1ull << ((int)ee / a.El));
+        } else if (b0 && i < nent && ee != -1) {
+            atomicOr(a.err, kErrBadTopk);
+        }
+    }
+    __syncthreads();
+    if (b0) {   // tokens per rank
+        for (int i = tid; i < T; i += kBlockThreads)
+            for (uint64_t m = tok_mask[i]; m != 0; m &= m - 1) atomicAdd(&tot[E + __ffsll((unsigned long long)m) - 1], 1);
+        __syncthreads();
+    }
+    const int total_e = block_exclusive_scan(tot, off, E, wsum);   // off[e] = entries with a smaller id
+    if (b0) {
+        const int total_r = block_exclusive_scan(tot + E, off + E, R, wsum);
+        for (int ee = tid; ee < E; ee += kBlockThreads) {
+            a.h_eoff[ee] = off[ee];
+            a.h_recv_counts[ee] = tot[ee];
+        }
+        for (int r = tid; r < R; r += kBlockThreads) a.h_roff[r] = off[E + r];
+        if (tid == 0) {
+            a.h_eoff[E] = total_e;
+            a.h_roff[R] = total_r;
+        }
+    }
+    if (!has_slice) return;
+
+    // ---- rank among the rows of its expert: earlier tokens + earlier slots of this token
+    int rank = 0, lessv = 0;
+    for (int j = 0; j < k; ++j) {
+        const int ej = readlane(e, j);
+        if (ej >= 0) {
+            const uint64_t m = __ballot(lane < k && e == ej);
+            if (lane == j) rank = __popcll(m & below);
+        }
+    }
+    if (e >= 0) {
+        rank += hb[e];
+        lessv = off[e];
+    }
+    int rrow = -1;
+    if (e >= 0) {
+        const int64_t row = (int64_t)e * a.cap + (int64_t)a.s0 * a.max_tokens + rank;
+        if (rank >= a.max_tokens || row >= a.recv_cap_rows) atomicOr(a.err, kErrBounds);
+        else rrow = (int)row;
+    }
+    if (s == 0 && lane < k) {
+        a.h_pos[(int64_t)t * k + lane] = rrow;
+        const int64_t cp = (int64_t)lessv + rank;   // expert-major position
+        if (rrow >= 0 && cp < a.pairs_cap) a.h_recv_src[cp] = t;
+    }
+
+    // ---- copy (and quantise) the slice into the token's slots
+    if constexpr (!FP8) {
+        for (int j = 0; j < k; ++j) {
+            const int rr = readlane(rrow, j);
+            if (rr >= 0) store_row<C>(reinterpret_cast<u32x4*>(a.recv_rows) + (int64_t)rr * nchunk, v, gbase, lane, nchunk);
+        }
+    } else {
+        u32x2 q[C];
+        float sinv[C];
+        quantize_slice<C>(v, q, sinv);
+        const int nbk = a.H / 128;
+        for (int j = 0; j < k; ++j) {
+            const int rr = readlane(rrow, j);
+            if (rr >= 0) {
+                store_row<C>(reinterpret_cast<u32x2*>(a.recv_rows) + (int64_t)rr * nchunk, q, gbase, lane, nchunk);
+                store_scales<C>(a.recv_scales + (int64_t)rr * nbk, sinv, g0, lane, nchunk);
             }
         }
     }
@@ -571,6 +744,24 @@ hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool se
         case 16: return pack_c<16>(a, fp8, ll, send, grid, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t s) {
+    const dim3 grid(a.T > 0 ? (unsigned)a.T : 1u);   // one block per token
+#define MOE_LL_CASE(CC)                                                                              \
+    case CC:                                                                                          \
+        if (fp8) hipLaunchKernelGGL((k_ll_dispatch<CC, true>), grid, dim3(kBlockThreads), 0, s, a);  \
+        else hipLaunchKernelGGL((k_ll_dispatch<CC, false>), grid, dim3(kBlockThreads), 0, s, a);     \
+        return hipGetLastError();
+    switch (chunks) {
+        MOE_LL_CASE(1)
+        MOE_LL_CASE(2)
+        MOE_LL_CASE(4)
+        MOE_LL_CASE(8)
+        MOE_LL_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef MOE_LL_CASE
 }
 
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s) {

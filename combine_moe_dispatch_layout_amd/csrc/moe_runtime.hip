@@ -370,7 +370,10 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
         return MOE_ERR_INVALID_ARG;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (!reuse_layout) {
+    // low latency without a reused layout: one fused launch when the routing is small
+    const bool fused = !reuse_layout && ll && (int64_t)num_tokens * c.topk <= kFusedMaxEntries &&
+                       num_tokens <= kFusedMaxTokens;
+    if (!reuse_layout && !fused) {
         moe_status st = run_layout(ctx, topk_idx, num_tokens, nullptr, nullptr, nullptr, s);
         if (st != MOE_OK) return st;
     }
@@ -417,7 +420,15 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     if (num_tokens == 0) a0.T = 0;
     TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH);
     hipError_t e;
-    if (num_tokens == 0) {
+    if (fused) {
+        // one block per token, its 4 wavefronts split the row into <= 4 slices
+        // (the context's layout state is neither read nor written here)
+        const int64_t nchunk = c.hidden / 8;
+        int cf = 1;
+        while (cf < 16 && (int64_t)kBlockThreads * cf < nchunk) cf *= 2;
+        a.nslices = (int)((nchunk + 64 * cf - 1) / (64 * cf));
+        e = launch_ll_fused(a, cf, fp8, s);
+    } else if (num_tokens == 0) {
         // grid of one block: block 0 copies the offsets, every wave exits (no items)
         a0.nslices = 1;
         e = launch_pack(a0, 1, fp8, ll, !ll, s);

@@ -211,7 +211,10 @@ typedef struct moe_handle {
 /* MoE dispatch (guide, "Core API example"; DeepTech article, feature list).
  *   x          bf16 [num_tokens, H] token hidden states
  *   topk_idx   int64 [num_tokens, k]; -1 = empty slot
- *   reuse_layout  0: compute the layout first (one extra kernel);
+ *   reuse_layout  0: compute the layout first (one extra kernel; in
+ *                    MOE_LAYOUT_PADDED_LL with num_tokens * topk <= 2048 and
+ *                    num_tokens <= 512 the
+ *                    routing and the copy run as one fused launch instead);
  *                 1: reuse the scan state of the last moe_dispatch_layout on this
  *                    context, which must have seen the same topk_idx pointer and
  *                    num_tokens (checked; the contents must not have changed)

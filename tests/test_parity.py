@@ -364,3 +364,107 @@ def test_expert_rank_extremes(gpu, E, R, k):
     x = W.to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
     run_case(gpu, c, x, idx, w, max_tokens=T, tag="extremes")
+
+
+# ---------------------------------------------------------------- fused low-latency dispatch
+# moe_dispatch without a reused layout in the padded low-latency mode runs the
+# routing and the copy as one launch when T * k <= 2048 and T <= 512; above
+# that it falls back to layout + pack.  Both must give the same results as the oracle.
+@pytest.mark.parametrize("quant", [W.QUANT_FP8, W.QUANT_BF16])
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 200, 255, 256, 257])
+def test_ll_fused_ragged(gpu, T, quant):
+    c = small_cfg("decode")
+    c["quant"] = quant
+    d = W.make("decode", T=T)
+    M = max(T, 1)
+    c["max_tokens"] = M
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), d["topk_idx"], d["topk_weights"], reuse=False,
+             max_tokens=M, tag="ll-fused-%d" % quant)
+
+
+@pytest.mark.parametrize("T,k", [(512, 4), (513, 2), (2048, 1), (64, 32), (65, 32), (1000, 2)])
+def test_ll_fused_topk_extremes(gpu, T, k):
+    c = dict(index=11, T=T, H=256, E=64, R=8, k=k, quant=W.QUANT_FP8,
+             layout=W.LAYOUT_PADDED_LL, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(T + k))
+    idx = W.route_uniform(rng, T, c["E"], k)
+    x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, T, k)
+    run_case(gpu, c, x, idx, w, reuse=False, max_tokens=T, tag="ll-fused-k%d" % k)
+
+
+def test_ll_fused_irregular_routing(gpu):
+    """Empty slots, a token with no expert, repeated experts in a row, bad ids,
+    a non-zero source rank."""
+    c = small_cfg("decode")
+    T = 128
+    d = W.make("decode", T=T)
+    idx = W.with_empty_slots(d["topk_idx"], 0.25)
+    idx[7, :] = -1
+    idx[9, :] = 17                     # one expert in every slot
+    idx[11, 3] = c["E"] + 5            # bad ids: flagged, treated as empty
+    idx[12, 0] = -9
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), idx, d["topk_weights"], reuse=False, max_tokens=T,
+             src_rank=5, tag="ll-fused-irregular")
+
+
+# ---------------------------------------------------------------- HIP graph capture
+@pytest.mark.parametrize("name,reuse", [("decode", False), ("prefill", True)])
+def test_graph_capture_replays_match_eager(gpu, name, reuse):
+    """The calls only enqueue kernels (no allocation, no memset, no sync), so a
+    step captures into a HIP graph.  Replay it several times, with eager work
+    and a synchronisation between replays, and check every replay against the
+    eager results."""
+    c = small_cfg(name)
+    T = 128 if name == "decode" else 700
+    d = W.make(name, T=T)
+    c["max_tokens"] = T
+    ctx = make_ctx(gpu, c, T, max_tokens=T)
+    x = to_dev_bf16(d["x"][:, :c["H"]].copy())
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    bufs = gpu.DispatchBuffers(ctx)
+    h = gpu.Handle(ctx)
+    n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
+    y = torch.randn((n_cap, c["H"]), device=dev()).to(torch.bfloat16)
+    out = torch.empty((T, c["H"]), dtype=torch.bfloat16, device=dev())
+    cnt_e = torch.empty(c["E"], dtype=torch.int32, device=dev())
+    cnt_r = torch.empty(c["R"], dtype=torch.int32, device=dev())
+    in_rank = torch.empty((T, c["R"]), dtype=torch.uint8, device=dev())
+
+    def step():
+        if reuse:
+            gpu.moe_dispatch_layout(ctx, idx, cnt_e, cnt_r, in_rank)
+        gpu.moe_dispatch(ctx, x, idx, reuse_layout=reuse, bufs=bufs, handle=h)
+        gpu.moe_combine(ctx, y, w, h, out=out)
+
+    watch = [out, h.pos, h.recv_src_idx, h.expert_offsets, h.recv_counts, bufs.recv_rows]
+    if bufs.recv_scales is not None:
+        watch.append(bufs.recv_scales)
+    if reuse:
+        watch += [cnt_e, cnt_r, in_rank, bufs.send_rows, h.send_src_idx, h.rank_offsets]
+    for t in watch:                           # same fill as between replays (unwritten rows stay equal)
+        t.view(torch.uint8).fill_(0x5A)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in watch]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in watch:                       # eager work between replays
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(watch, eager)):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), ("replay", rep, "tensor", i)
+    st, _ = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK
+    del g
+    ctx.close()
