@@ -49,6 +49,10 @@ def _bind(path):
     lib.orc_dispatch_rows.argtypes = [_vp, _i32, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
     lib.orc_combine.restype = None
     lib.orc_combine.argtypes = [_vp, _i32, _vp, _vp, _i64, _i32, _vp]
+    lib.orc_dispatch_backward.restype = None
+    lib.orc_dispatch_backward.argtypes = [_vp, _i32, _vp, _i64, _i32, _vp]
+    lib.orc_combine_backward.restype = None
+    lib.orc_combine_backward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]
     for name in ("orc_f32_to_e4m3_n", "orc_e4m3_to_f32_n", "orc_f32_to_bf16_n", "orc_bf16_to_f32_n"):
         f = getattr(lib, name)
         f.restype = None
@@ -190,3 +194,45 @@ def combine(y_bf16, topk_weights, pos):
     out = np.empty((T, H), np.uint16)
     _load().orc_combine(_p(y), H, _p(w), _p(pos), T, k, _p(out))
     return out
+
+
+# ---------------------------------------------------------------- backward
+def _check_pos(pos, rows):
+    if pos.size:
+        valid = pos[pos >= 0]
+        if valid.size and valid.max() >= rows:
+            raise IndexError("oracle: pos beyond the receive rows")
+
+
+def dispatch_backward(grad_recv_bf16, pos):
+    """grad_x[t] = bf16(sum over valid j, ascending, of grad_recv[pos[t, j]]),
+    binary32 from +0 (the adjoint of dispatch's copy into the receive rows)."""
+    g = _c(grad_recv_bf16, np.uint16)
+    pos = _c(pos, np.int32)
+    T, k = pos.shape
+    H = g.shape[1]
+    _check_pos(pos, g.shape[0])
+    out = np.empty((T, H), np.uint16)
+    _load().orc_dispatch_backward(_p(g), H, _p(pos), T, k, _p(out))
+    return out
+
+
+def combine_backward(grad_out_bf16, topk_weights, y_bf16, pos, grad_y=None):
+    """Gradients of combine: grad_y rows at pos = bf16(w * grad_out) (binary32
+    product), grad_w[t, j] = <grad_out[t], y[pos[t, j]]> (binary64, float64
+    result).  grad_y: optional uint16 [rows, H] array updated in place (rows no
+    slot points at keep their contents); by default a zero array the size of y."""
+    go = _c(grad_out_bf16, np.uint16)
+    w = _c(topk_weights, np.float32)
+    y = _c(y_bf16, np.uint16)
+    pos = _c(pos, np.int32)
+    T, k = pos.shape
+    H = go.shape[1]
+    assert y.shape[1] == H and go.shape[0] == T
+    _check_pos(pos, y.shape[0])
+    if grad_y is None:
+        grad_y = np.zeros(y.shape, np.uint16)
+    assert grad_y.dtype == np.uint16 and grad_y.flags.c_contiguous and grad_y.shape == y.shape
+    grad_w = np.empty((T, k), np.float64)
+    _load().orc_combine_backward(_p(go), _p(w), _p(y), _p(pos), T, k, H, _p(grad_y), _p(grad_w))
+    return grad_y, grad_w

@@ -321,3 +321,68 @@ void orc_combine(const uint16_t* y, int H, const float* w, const int32_t* pos,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass.  The DeepTech release article's feature list names
+ * high-throughput kernels for training; training needs the gradients of
+ * dispatch and combine.  The pages give no formulas for them, so these are the
+ * derivatives of the forward definitions above:
+ *  - dispatch copies x[t] into receive row pos[t, j] for every valid slot j;
+ *    the adjoint of that copy adds the gradients of those rows back into
+ *    token t.  FP8 quantisation is passed through as the identity (its codes
+ *    times the stored scale reproduce x up to rounding).
+ *  - combine is linear in the expert outputs and in the weights:
+ *    d out[t] / d y[pos[t, j]] = w[t, j] and d out[t] / d w[t, j] =
+ *    y[pos[t, j]].  Its final bf16 rounding is passed through as the identity.
+ * Gradients travel in bf16 like the forward combine's inputs and outputs. */
+
+/* Dispatch backward:
+ *   grad_x[t, h] = bf16_rne( sum over valid j, ascending, of g[pos[t, j], h] )
+ * summed in binary32 from +0, one addition at a time (the forward combine's
+ * accumulation with every weight equal to one).  Empty slots contribute
+ * nothing; a token with no valid slot gets +0. */
+void orc_dispatch_backward(const uint16_t* g, int H, const int32_t* pos,
+                           int64_t T, int k, uint16_t* grad_x)
+{
+    for (int64_t t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; j++) {
+                int32_t p = pos[t * k + j];
+                if (p >= 0) acc = acc + orc_bf16_to_f32(g[(int64_t)p * H + h]);
+            }
+            grad_x[t * H + h] = orc_f32_to_bf16(acc);
+        }
+    }
+}
+
+/* Combine backward, with go = the gradient of combine's output [T, H]:
+ *   grad_y[pos[t, j], h] = bf16_rne( w[t, j] * go[t, h] ) for every valid slot,
+ *       the product rounded to binary32 first, as in the forward combine;
+ *       rows of grad_y that no slot points at are not written.
+ *   grad_w[t, j] = sum over h of go[t, h] * y[pos[t, j], h], 0 for an empty
+ *       slot.  Each product of two bf16 values is exact in binary64 and the
+ *       sum is taken in binary64, so the result is the exact dot product to
+ *       within H * 2^-53 of the sum of |terms|. */
+void orc_combine_backward(const uint16_t* go, const float* w, const uint16_t* y,
+                          const int32_t* pos, int64_t T, int k, int H,
+                          uint16_t* grad_y, double* grad_w)
+{
+    for (int64_t t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            int32_t p = pos[t * k + j];
+            if (p < 0) {
+                grad_w[t * k + j] = 0.0;
+                continue;
+            }
+            double dot = 0.0;
+            for (int h = 0; h < H; h++) {
+                float gv = orc_bf16_to_f32(go[t * H + h]);
+                float prod = w[t * k + j] * gv;
+                grad_y[(int64_t)p * H + h] = orc_f32_to_bf16(prod);
+                dot += (double)gv * (double)orc_bf16_to_f32(y[(int64_t)p * H + h]);
+            }
+            grad_w[t * k + j] = dot;
+        }
+    }
+}

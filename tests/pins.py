@@ -377,3 +377,190 @@ def check_dispatch_rows(orc, x_bits, idx, E, R, quant):
         assert np.array_equal(d["send_scales"], s[d["send_src_idx"]])
         assert np.array_equal(d["recv_scales"], s[d["recv_src_idx"]])
     return d
+
+
+# ----------------------------------------------------------------------------
+# backward pass
+def _bf16_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def small_int_bf16(rng, shape, lo=-4, hi=4):
+    """bf16 bit patterns of small integers: every sum and product the backward
+    pins form from them is exact in binary32 and binary64."""
+    v = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return f32_to_bf16_torch(v)
+
+
+def check_dispatch_backward_bound(orc, g_bits, pos):
+    """grad_x against the exact binary64 sum of the routed gradient rows: within
+    the binary32 recursive-summation bound plus the final bf16 rounding, and
+    within one bf16 ulp wherever the summation error is negligible."""
+    T, k = pos.shape
+    H = g_bits.shape[1]
+    out = orc.dispatch_backward(g_bits, pos)
+    g = _bf16_f64(g_bits)
+    exact = np.zeros((T, H))
+    mag = np.zeros((T, H))
+    for j in range(k):
+        p = pos[:, j]
+        v = p >= 0
+        exact[v] += g[p[v]]
+        mag[v] += np.abs(g[p[v]])
+    gamma = (k + 1) * 2.0 ** -24 * (1 + 2.0 ** -20)
+    o = _bf16_f64(out)
+    bound = 2.0 ** -8 * (np.abs(exact) + gamma * mag) + gamma * mag + 2.0 ** -133
+    assert np.all(np.abs(o - exact) <= bound), "dispatch backward outside the summation bound"
+    ref = f32_to_bf16_torch(exact.astype(np.float32))
+    d = np.abs(bf16_ordered(out) - bf16_ordered(ref))
+    clean = gamma * mag <= 2.0 ** -11 * np.abs(exact)
+    assert clean.mean() > 0.95
+    assert d[clean].max(initial=0) <= 1, "dispatch backward further than 1 bf16 ulp from the exact sum"
+    has = (pos >= 0).any(axis=1)
+    assert np.all(out[~has] == 0), "token without experts -> +0 gradient"
+    return out
+
+
+def check_dispatch_backward_adjoint(orc, idx, E, R, rng, H=256):
+    """<dispatch(x), g> over the receive rows equals <x, dispatch_backward(g)>
+    over the tokens (the defining property of an adjoint), on small-integer data
+    where both sides are exact; with k = 1 the backward is a plain gather."""
+    T, k = idx.shape
+    x = small_int_bf16(rng, (T, H))
+    d = orc.dispatch(x, idx, E, R, quant=0)
+    n = d["n_pairs"]
+    g = small_int_bf16(rng, (max(n, 1), H))
+    gx = orc.dispatch_backward(g, d["pos"])
+    lhs = float((_bf16_f64(d["recv_rows"]) * _bf16_f64(g[:n])).sum()) if n else 0.0
+    rhs = float((_bf16_f64(x) * _bf16_f64(gx)).sum())
+    assert lhs == rhs, "dispatch backward is not the adjoint of dispatch (%r vs %r)" % (lhs, rhs)
+    one = d["pos"][:, :1].copy()
+    g1 = orc.dispatch_backward(g, one)
+    v = one[:, 0] >= 0
+    assert np.array_equal(g1[v], g[one[v, 0]]), "single slot: backward is a gather"
+
+
+def check_combine_backward_bounds(orc, go_bits, w, y_bits, pos):
+    """grad_y: each routed row is w * grad_out rounded to binary32 then bf16
+    (within 2^-8 relative plus binary32 rounding); w = 1 and w = -2 are exact
+    (bit copy, sign flip and exponent step).  grad_w: within H * 2^-50 of the
+    binary64 matrix product of grad_out and the routed rows.  Rows no slot
+    points at are left alone; empty slots get grad_w = 0."""
+    T, k = pos.shape
+    rows, H = y_bits.shape
+    sentinel = np.full((rows, H), 0x5A5A, np.uint16)
+    gy, gw = orc.combine_backward(go_bits, w, y_bits, pos, grad_y=sentinel.copy())
+    go = _bf16_f64(go_bits)
+    y = _bf16_f64(y_bits)
+    hit = np.zeros(rows, bool)
+    for j in range(k):
+        p = pos[:, j]
+        v = p >= 0
+        hit[p[v]] = True
+        prod = w[v, j].astype(np.float64)[:, None] * go[v]
+        err = np.abs(_bf16_f64(gy[p[v]]) - prod)
+        # binary32 rounding (2^-24 relative), then bf16 rounding (unit roundoff 2^-8)
+        assert np.all(err <= (2.0 ** -8 + 2.0 ** -23) * np.abs(prod) + 2.0 ** -133), \
+            "grad_y is not the rounded weighted gradient"
+        # binary64 matrix product (BLAS) of the token's gradient with its routed rows
+        ref = np.einsum("th,th->t", go[v], y[p[v]])
+        mag = np.einsum("th,th->t", np.abs(go[v]), np.abs(y[p[v]]))
+        assert np.all(np.abs(gw[v, j] - ref) <= H * 2.0 ** -50 * mag + 1e-300), "grad_w is not the dot product"
+        assert np.all(gw[~v, j] == 0.0), "empty slot -> grad_w = 0"
+    assert np.all(gy[~hit] == 0x5A5A), "combine backward wrote a row no slot points at"
+    # w = 3/4: the binary32 product is exact, so grad_y is torch's RNE cast of it
+    gy34, _ = orc.combine_backward(go_bits, np.full_like(w, 0.75), y_bits, pos)
+    for j in range(k):
+        p = pos[:, j]
+        v = p >= 0
+        assert np.array_equal(gy34[p[v]], f32_to_bf16_torch((0.75 * go[v]).astype(np.float32))), \
+            "grad_y with w = 3/4 is not the correctly rounded product"
+    # exact special weights
+    for wv in (1.0, -2.0):
+        gy1, _ = orc.combine_backward(go_bits, np.full_like(w, wv), y_bits, pos)
+        for j in range(k):
+            p = pos[:, j]
+            v = p >= 0
+            assert np.array_equal(_bf16_f64(gy1[p[v]]), wv * go[v]), "grad_y with w = %g" % wv
+    return gy, gw
+
+
+def check_combine_backward_closed_form(orc, rng):
+    """Constant rows: grad_out[t] = c_t, y row = d_r, so grad_w[t, j] = H c_t d_r."""
+    T, k, H = 6, 3, 384
+    rows = T * k
+    pos = np.arange(rows, dtype=np.int32).reshape(T, k)[:, ::-1].copy()
+    pos[2, 1] = -1
+    c = rng.integers(-3, 4, size=T).astype(np.float32) / 4
+    d = rng.integers(-5, 6, size=rows).astype(np.float32) / 8
+    go = f32_to_bf16_torch(np.repeat(c[:, None], H, axis=1))
+    y = f32_to_bf16_torch(np.repeat(d[:, None], H, axis=1))
+    w = rng.standard_normal((T, k)).astype(np.float32)
+    _, gw = orc.combine_backward(go, w, y, pos)
+    for t in range(T):
+        for j in range(k):
+            p = pos[t, j]
+            want = 0.0 if p < 0 else H * float(c[t]) * float(d[p])
+            assert gw[t, j] == want, "grad_w closed form at (%d, %d)" % (t, j)
+
+
+def check_backward_finite_differences(orc, rng):
+    """Brute force on a tiny case: the loss L(w, y) = sum_t <go[t], sum_j
+    w[t, j] y[pos[t, j]]> in binary64, differentiated by central differences
+    in every weight and every expert-output entry (exact here: L is linear in
+    each, the data are small integers), must equal grad_w and, for w = 1,
+    grad_y.  Dispatch backward against the differences of <dispatch(x), g> in
+    every x entry."""
+    T, k, H, rows = 4, 2, 8, 9
+    pos = np.array([[3, 0], [5, -1], [8, 1], [2, 7]], np.int32)
+    go = small_int_bf16(rng, (T, H))
+    y = small_int_bf16(rng, (rows, H))
+    w = (rng.integers(-4, 5, size=(T, k)) / 4).astype(np.float32)
+
+    def loss(wv, yv):
+        s = 0.0
+        for t in range(T):
+            for j in range(k):
+                if pos[t, j] >= 0:
+                    for h in range(H):
+                        s += float(go_f[t, h]) * float(wv[t, j]) * float(yv[pos[t, j], h])
+        return s
+
+    go_f, y_f = _bf16_f64(go), _bf16_f64(y)
+    _, gw = orc.combine_backward(go, w, y, pos)
+    w_f = w.astype(np.float64)
+    for t in range(T):
+        for j in range(k):
+            wp, wm = w_f.copy(), w_f.copy()
+            wp[t, j] += 1.0
+            wm[t, j] -= 1.0
+            assert gw[t, j] == (loss(wp, y_f) - loss(wm, y_f)) / 2, "grad_w finite difference (%d, %d)" % (t, j)
+    gy, _ = orc.combine_backward(go, np.ones_like(w), y, pos)
+    ones = np.ones((T, k))
+    for r in set(pos[pos >= 0].tolist()):
+        for h in range(H):
+            yp, ym = y_f.copy(), y_f.copy()
+            yp[r, h] += 1.0
+            ym[r, h] -= 1.0
+            assert _bf16_f64(gy[r:r + 1, h:h + 1])[0, 0] == (loss(ones, yp) - loss(ones, ym)) / 2, \
+                "grad_y finite difference (%d, %d)" % (r, h)
+    # dispatch: L(x) = <dispatch(x) receive rows, g>, through the forward oracle
+    idx = np.array([[3, 0], [5, -1], [7, 1], [2, 3]], np.int64)
+    x = small_int_bf16(rng, (T, H))
+    fwd = orc.dispatch(x, idx, 8, 2, quant=0)
+    g = small_int_bf16(rng, (fwd["n_pairs"], H))
+    g_f = _bf16_f64(g)
+
+    def dloss(xb):
+        return float((_bf16_f64(orc.dispatch(xb, idx, 8, 2, quant=0)["recv_rows"]) * g_f).sum())
+
+    gx = _bf16_f64(orc.dispatch_backward(g, fwd["pos"]))
+    x_f = _bf16_f64(x)
+    for t in range(T):
+        for h in range(H):
+            xp, xm = x_f.copy(), x_f.copy()
+            xp[t, h] += 1.0
+            xm[t, h] -= 1.0
+            fd = (dloss(f32_to_bf16_torch(xp.astype(np.float32))) -
+                  dloss(f32_to_bf16_torch(xm.astype(np.float32)))) / 2
+            assert gx[t, h] == fd, "dispatch backward finite difference (%d, %d)" % (t, h)

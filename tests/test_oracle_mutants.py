@@ -43,11 +43,36 @@ MUTANTS = [
     ("quant_stored_scale_inverse", "scales[b] = sinv;", "scales[b] = s;"),
     ("quant_block_shift", "float prod = orc_bf16_to_f32(x[b * 128 + i]) * s;",
      "float prod = orc_bf16_to_f32(x[b * 128 + (i + 1) % 128]) * s;"),
-    ("combine_weights_transposed", "float prod = w[t * k + j]", "float prod = w[(j * T + t) % (T * k)]"),
+    ("combine_weights_transposed", "float prod = w[t * k + j] * orc_bf16_to_f32(y",
+     "float prod = w[(j * T + t) % (T * k)] * orc_bf16_to_f32(y"),
     ("combine_wrong_sign", "acc = acc + prod;", "acc = acc - prod;"),
-    ("combine_dropped_term", "for (int j = 0; j < k; j++) {\n                int32_t p = pos[t * k + j];",
-     "for (int j = 1; j < k; j++) {\n                int32_t p = pos[t * k + j];"),
-    ("combine_start_not_zero", "float acc = 0.0f;", "float acc = 1e-3f;"),
+    ("combine_dropped_term", "for (int j = 0; j < k; j++) {\n                int32_t p = pos[t * k + j];\n"
+     "                if (p < 0) continue;",
+     "for (int j = 1; j < k; j++) {\n                int32_t p = pos[t * k + j];\n"
+     "                if (p < 0) continue;"),
+    ("combine_start_not_zero", "float acc = 0.0f;\n            for (int j = 0; j < k; j++) {\n"
+     "                int32_t p = pos[t * k + j];\n                if (p < 0)",
+     "float acc = 1e-3f;\n            for (int j = 0; j < k; j++) {\n"
+     "                int32_t p = pos[t * k + j];\n                if (p < 0)"),
+    ("dispatch_bwd_dropped_term", "if (p >= 0) acc = acc + orc_bf16_to_f32(g[",
+     "if (p >= 0 && j > 0) acc = acc + orc_bf16_to_f32(g["),
+    ("dispatch_bwd_wrong_sign", "acc = acc + orc_bf16_to_f32(g[", "acc = acc - orc_bf16_to_f32(g["),
+    ("dispatch_bwd_token_row", "orc_bf16_to_f32(g[(int64_t)p * H + h])", "orc_bf16_to_f32(g[(int64_t)t * H + h])"),
+    ("dispatch_bwd_start_not_zero", "float acc = 0.0f;\n            for (int j = 0; j < k; j++) {\n"
+     "                int32_t p = pos[t * k + j];\n                if (p >= 0)",
+     "float acc = 1e-3f;\n            for (int j = 0; j < k; j++) {\n"
+     "                int32_t p = pos[t * k + j];\n                if (p >= 0)"),
+    ("combine_bwd_no_weight", "float prod = w[t * k + j] * gv;", "float prod = gv;"),
+    ("combine_bwd_weight_transposed", "float prod = w[t * k + j] * gv;",
+     "float prod = w[(j * T + t) % (T * k)] * gv;"),
+    ("combine_bwd_grad_y_truncated", "grad_y[(int64_t)p * H + h] = orc_f32_to_bf16(prod);",
+     "grad_y[(int64_t)p * H + h] = (uint16_t)(f32_bits(prod) >> 16);"),
+    ("combine_bwd_grad_w_weighted", "dot += (double)gv * (double)orc_bf16_to_f32(y[",
+     "dot += (double)prod * (double)orc_bf16_to_f32(y["),
+    ("combine_bwd_grad_w_shifted", "(double)orc_bf16_to_f32(y[(int64_t)p * H + h]);",
+     "(double)orc_bf16_to_f32(y[(int64_t)p * H + (h + 1) % H]);"),
+    ("combine_bwd_grad_w_float", "double dot = 0.0;", "float dot = 0.0f;"),
+    ("combine_bwd_empty_slot", "grad_w[t * k + j] = 0.0;", "grad_w[t * k + j] = -1.0;"),
     ("dispatch_wrong_source", "const uint16_t* xr = x + (int64_t)src[i] * H;",
      "const uint16_t* xr = x + (int64_t)src[n - 1 - i] * H;"),
 ]
@@ -96,6 +121,13 @@ def run_all_pins(orc):
     y = W.expert_outputs(d, pp["n_pairs"])
     pins.check_combine(orc, y, d["topk_weights"], pp["pos"])
     pins.check_identity_roundtrip(orc, d["x"], d["topk_idx"], d["topk_weights"], c["E"], c["R"])
+    g = W.grad_rows(d, pp["n_pairs"])
+    pins.check_dispatch_backward_bound(orc, g, pp["pos"])
+    pins.check_dispatch_backward_adjoint(orc, W.with_empty_slots(idx, 0.25), 32, 4, rng)
+    go = W.grad_rows(d, 64)
+    pins.check_combine_backward_bounds(orc, go, d["topk_weights"], y, pp["pos"])
+    pins.check_combine_backward_closed_form(orc, rng)
+    pins.check_backward_finite_differences(orc, rng)
 
 
 def test_real_oracle_passes_compact_pins(orc):

@@ -162,3 +162,67 @@ def test_pages_settings_fixture():
     assert c["k"] == int(vals["production.topk"]) == int(vals["ampere.num_topk"])
     assert vals["production.dispatch_dtype"] == "fp8" and c["quant"] == W.QUANT_FP8
     assert vals["production.combine_dtype"] == "bf16"
+
+
+# ---------------------------------------------------------------- backward
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("decode", 128), ("skewed", 300)])
+def test_dispatch_backward(orc, name, T):
+    d = W.make(name, T=T)
+    c = d["cfg"]
+    for idx in (d["topk_idx"], W.with_empty_slots(d["topk_idx"], 0.3)):
+        pp = orc.positions(idx, c["E"], c["R"], orc.layout(idx, c["E"], c["R"]))
+        g = W.grad_rows(d, max(pp["n_pairs"], 1))
+        pins.check_dispatch_backward_bound(orc, g, pp["pos"])
+        # unit weights: the same reduction as the (pinned) combine
+        assert np.array_equal(orc.dispatch_backward(g, pp["pos"]),
+                              orc.combine(g, np.ones(pp["pos"].shape, np.float32), pp["pos"]))
+
+
+@pytest.mark.parametrize("T,k,E,R", [(1, 1, 4, 1), (40, 3, 12, 3), (200, 8, 64, 8)])
+def test_dispatch_backward_adjoint(orc, T, k, E, R):
+    rng = np.random.Generator(np.random.PCG64(100 + T))
+    idx = W.route_uniform(rng, T, E, k)
+    pins.check_dispatch_backward_adjoint(orc, idx, E, R, rng)
+    pins.check_dispatch_backward_adjoint(orc, W.with_empty_slots(idx, 0.25), E, R, rng)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("decode", 64), ("skewed", 200)])
+def test_combine_backward(orc, name, T):
+    d = W.make(name, T=T)
+    c = d["cfg"]
+    idx = W.with_empty_slots(d["topk_idx"], 0.2)
+    pp = orc.positions(idx, c["E"], c["R"], orc.layout(idx, c["E"], c["R"]))
+    y = W.expert_outputs(d, max(pp["n_pairs"], 1) + 3)   # 3 rows no slot points at
+    go = W.grad_rows(d, T)
+    pins.check_combine_backward_bounds(orc, go, d["topk_weights"], y, pp["pos"])
+
+
+def test_combine_backward_adjoint(orc):
+    """sum_{t,j} w[t,j] grad_w[t,j] = sum_t <go[t], sum_j w[t,j] y[pos]> =
+    <grad_y, y> over the routed rows, exact on small-integer data."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    T, k, E, R, H = 50, 4, 16, 4, 256
+    idx = W.with_empty_slots(W.route_uniform(rng, T, E, k), 0.2)
+    pp = orc.positions(idx, E, R, orc.layout(idx, E, R))
+    n = pp["n_pairs"]
+    y = pins.small_int_bf16(rng, (n, H))
+    go = pins.small_int_bf16(rng, (T, H))
+    w = (rng.integers(-8, 9, size=(T, k)) / 8).astype(np.float32)
+    gy, gw = orc.combine_backward(go, w, y, pp["pos"])
+    yf, gof = pins._bf16_f64(y), pins._bf16_f64(go)
+    fwd = np.zeros((T, H))
+    for j in range(k):
+        v = pp["pos"][:, j] >= 0
+        fwd[v] += w[v, j].astype(np.float64)[:, None] * yf[pp["pos"][v, j]]
+    a = float((w.astype(np.float64) * gw).sum())
+    b = float((gof * fwd).sum())
+    cc = float((pins._bf16_f64(gy) * yf).sum())
+    assert a == b == cc
+
+
+def test_combine_backward_closed_form(orc):
+    pins.check_combine_backward_closed_form(orc, np.random.Generator(np.random.PCG64(5)))
+
+
+def test_backward_finite_differences(orc):
+    pins.check_backward_finite_differences(orc, np.random.Generator(np.random.PCG64(6)))

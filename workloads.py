@@ -48,9 +48,11 @@ WORKLOADS = {
 
 
 def streams(index, extra=0):
-    """Four independent generators [x, routing, weights, expert_out]."""
+    """Five independent generators [x, routing, weights, expert_out, grads].
+    (Children of one SeedSequence: the first four do not depend on how many
+    are spawned.)"""
     ss = np.random.SeedSequence(SEED_BASE + index + 1000 * extra)
-    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(4)]
+    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
 
 
 def to_bf16_bits(a):
@@ -125,7 +127,7 @@ def make(name, T=None, extra_seed=0):
         cfg["T"] = T
         cfg["max_tokens"] = max(cfg["max_tokens"], T)
     T, H, E, k = cfg["T"], cfg["H"], cfg["E"], cfg["k"]
-    rx, rr, rw, _ = streams(cfg["index"], extra_seed)
+    rx, rr, rw = streams(cfg["index"], extra_seed)[:3]
     x = to_bf16_bits(rx.standard_normal((T, H), dtype=np.float32))
     if cfg["routing"] == "uniform":
         idx = route_uniform(rr, T, E, k)
@@ -149,6 +151,14 @@ def expert_outputs(inputs, n_rows):
     rng = streams(cfg["index"], cfg.get("extra_seed", 0))[3]
     H = cfg["H"]
     return to_bf16_bits(rng.standard_normal((n_rows, H), dtype=np.float32))
+
+
+def grad_rows(inputs, n_rows):
+    """Independent N(0,1) bf16 gradient rows, n_rows x H (the gradient of the
+    combine output, or of the dispatched receive rows), from their own stream."""
+    cfg = inputs["cfg"]
+    rng = streams(cfg["index"], cfg.get("extra_seed", 0))[4]
+    return to_bf16_bits(rng.standard_normal((n_rows, cfg["H"]), dtype=np.float32))
 
 
 def with_empty_slots(idx, frac, seed=7):
