@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     MOE_BUF_LAYOUT_TOKEN_IN_RANK, MOE_BUF_RECV_ROWS, MOE_BUF_RECV_SCALES, MOE_BUF_SEND_ROWS,
     MOE_BUF_SEND_SCALES, MOE_BUF_WORKSPACE, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY,
     MOE_ERR_DEVICE_BOUNDS, MOE_ERR_HANDLE, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
-    MOE_KERNEL_COMBINE, MOE_KERNEL_DISPATCH, MOE_KERNEL_LAYOUT, MOE_LAYOUT_CONTIGUOUS,
-    MOE_LAYOUT_PADDED_LL, MOE_OK, MOE_QUANT_BF16, MOE_QUANT_FP8_E4M3, load_library, make_config,
-    moe_combine, moe_dispatch, moe_dispatch_layout, moe_poll_error, moe_size_hint, status_str)
+    MOE_KERNEL_COMBINE, MOE_KERNEL_COMBINE_BWD, MOE_KERNEL_DISPATCH, MOE_KERNEL_DISPATCH_BWD,
+    MOE_KERNEL_LAYOUT, MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_PADDED_LL, MOE_OK, MOE_QUANT_BF16,
+    MOE_QUANT_FP8_E4M3, load_library, make_config, moe_combine, moe_combine_backward, moe_dispatch,
+    moe_dispatch_backward, moe_dispatch_layout, moe_poll_error, moe_size_hint, status_str)

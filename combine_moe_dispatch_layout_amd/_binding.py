@@ -34,8 +34,9 @@ MOE_LAYOUT_PADDED_LL = 1
  MOE_BUF_LAYOUT_EXPERT_COUNTS, MOE_BUF_LAYOUT_RANK_COUNTS, MOE_BUF_LAYOUT_TOKEN_IN_RANK,
  MOE_BUF_WORKSPACE) = range(16)
 
-MOE_KERNEL_LAYOUT, MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE = 0, 1, 2
-KERNEL_NAMES = ("layout", "dispatch", "combine")
+(MOE_KERNEL_LAYOUT, MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE, MOE_KERNEL_DISPATCH_BWD,
+ MOE_KERNEL_COMBINE_BWD) = range(5)
+KERNEL_NAMES = ("layout", "dispatch", "combine", "dispatch_bwd", "combine_bwd")
 
 
 class MoeError(RuntimeError):
@@ -66,8 +67,8 @@ class moe_handle(ctypes.Structure):
 
 # the full list of symbols include/moe_ep.h declares
 EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy", "moe_ctx_config",
-           "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_poll_error",
-           "moe_timing_begin", "moe_timing_end")
+           "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_backward",
+           "moe_combine_backward", "moe_poll_error", "moe_timing_begin", "moe_timing_end")
 
 _lib = None
 
@@ -94,6 +95,8 @@ def load_library(path=LIB_PATH):
         "moe_dispatch": [vp, vp, vp, i32, i32, ctypes.POINTER(moe_dispatch_buffers),
                          ctypes.POINTER(moe_handle), vp],
         "moe_combine": [vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp],
+        "moe_dispatch_backward": [vp, vp, ctypes.POINTER(moe_handle), vp, vp],
+        "moe_combine_backward": [vp, vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp, vp],
         "moe_poll_error": [vp, vp, u32p],
         "moe_timing_begin": [vp, i32],
         "moe_timing_end": [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
@@ -173,10 +176,11 @@ class Context:
         _check(load_library().moe_timing_begin(self.handle, max_launches), "moe_timing_begin")
 
     def timing_end(self):
-        tot = (ctypes.c_double * 3)()
-        cnt = (ctypes.c_int64 * 3)()
+        n = len(KERNEL_NAMES)
+        tot = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
         _check(load_library().moe_timing_end(self.handle, tot, cnt), "moe_timing_end")
-        return {KERNEL_NAMES[i]: {"total_ms": tot[i], "launches": cnt[i]} for i in range(3)}
+        return {KERNEL_NAMES[i]: {"total_ms": tot[i], "launches": cnt[i]} for i in range(n)}
 
 
 class Handle:
@@ -287,6 +291,54 @@ def moe_combine(ctx, expert_out, topk_weights, handle, out=None):
     _check(load_library().moe_combine(ctx.handle, _ptr(expert_out), _ptr(topk_weights),
                                       ctypes.byref(handle.c), _ptr(out), _stream()), "moe_combine")
     return out
+
+
+def moe_dispatch_backward(ctx, grad_recv, handle, grad_x=None):
+    """Gradient of dispatch: grad_x bf16 [T, H] from the receive-layout
+    gradient rows (bf16, at least MOE_BUF_EXPERT_OUT bytes)."""
+    c = ctx.cfg
+    _as_dev(grad_recv, torch.bfloat16, "grad_recv")
+    if grad_recv.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
+        raise ValueError("grad_recv smaller than MOE_BUF_EXPERT_OUT")
+    T = handle.num_tokens
+    if grad_x is None:
+        grad_x = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=grad_recv.device)
+    _as_dev(grad_x, torch.bfloat16, "grad_x")
+    if grad_x.numel() < T * c.hidden:
+        raise ValueError("grad_x must hold [T, %d]" % c.hidden)
+    _check(load_library().moe_dispatch_backward(ctx.handle, _ptr(grad_recv), ctypes.byref(handle.c),
+                                                _ptr(grad_x), _stream()), "moe_dispatch_backward")
+    return grad_x
+
+
+def moe_combine_backward(ctx, grad_out, topk_weights, expert_out, handle, grad_expert_out=None,
+                         grad_weights=None):
+    """Gradients of combine: returns (grad_expert_out bf16 in the receive layout,
+    grad_weights fp32 [T, k])."""
+    c = ctx.cfg
+    T = handle.num_tokens
+    _as_dev(grad_out, torch.bfloat16, "grad_out")
+    _as_dev(topk_weights, torch.float32, "topk_weights")
+    _as_dev(expert_out, torch.bfloat16, "expert_out")
+    if tuple(topk_weights.shape) != (T, c.topk) or grad_out.numel() < T * c.hidden:
+        raise ValueError("topk_weights must be [T, %d] and grad_out [T, %d]" % (c.topk, c.hidden))
+    if expert_out.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
+        raise ValueError("expert_out smaller than MOE_BUF_EXPERT_OUT")
+    if grad_expert_out is None:
+        grad_expert_out = torch.empty_like(expert_out)
+    _as_dev(grad_expert_out, torch.bfloat16, "grad_expert_out")
+    if grad_expert_out.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
+        raise ValueError("grad_expert_out smaller than MOE_BUF_EXPERT_OUT")
+    if grad_weights is None:
+        grad_weights = torch.empty((T, c.topk), dtype=torch.float32, device=grad_out.device)
+    _as_dev(grad_weights, torch.float32, "grad_weights")
+    if grad_weights.numel() < T * c.topk:
+        raise ValueError("grad_weights must hold [T, %d]" % c.topk)
+    _check(load_library().moe_combine_backward(ctx.handle, _ptr(grad_out), _ptr(topk_weights),
+                                               _ptr(expert_out), ctypes.byref(handle.c),
+                                               _ptr(grad_expert_out), _ptr(grad_weights), _stream()),
+           "moe_combine_backward")
+    return grad_expert_out, grad_weights
 
 
 def moe_poll_error(ctx):

@@ -77,7 +77,7 @@ struct PackArgs {
 
 struct CombineArgs {
     const uint16_t* y;         // bf16 expert outputs in the receive layout
-    const float* w;            // [T, k]
+    const float* w;            // [T, k]; nullptr = every weight 1 (dispatch backward)
     const int32_t* pos;        // [T, k]
     uint16_t* out;             // bf16 [T, H]
     int32_t T, k, H;
@@ -86,11 +86,27 @@ struct CombineArgs {
     uint32_t* err;
 };
 
+struct CombineBwdArgs {
+    const uint16_t* go;        // bf16 [T, H] gradient of the combine output
+    const float* w;            // [T, k]
+    const uint16_t* y;         // bf16 expert outputs in the receive layout
+    const int32_t* pos;        // [T, k]
+    uint16_t* gy;              // bf16 gradient of the expert outputs (rows at pos)
+    float* gw;                 // [T, k] gradient of the weights
+    float* part;               // [T, nslices, k] partial dot products (nslices > 1)
+    uint32_t* arrive;          // [T] arrival counters, zero between launches
+    int32_t T, k, H;
+    int32_t nslices;
+    int64_t rows_cap;
+    uint32_t* err;
+};
+
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
 hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s);
 // chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16)
 hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s);
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, hipStream_t s);
 // Low-latency dispatch without a separate layout launch (T * k <= kFusedMaxEntries).
 hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t s);
 

@@ -24,7 +24,13 @@
 //    expert outputs are read exactly once, so they use non-temporal loads
 //    (measured ~35% faster than cached loads here); short slices (2 chunks per
 //    lane) keep many small wavefronts in flight.
-// There is no contraction to put on MFMA.
+//  * Backward: dispatch backward is the combine kernel with unit weights (the
+//    adjoint of copying a token to k rows is adding those k rows back).  The
+//    combine backward kernel has combine's shape: it reads the output gradient
+//    and the k routed expert-output rows once, writes the weighted gradient to
+//    each routed row, and reduces one dot product per slot for grad_w.
+// There is no contraction to put on MFMA: the grad_w dot products are one
+// multiply-add per loaded element (k of them per 16-byte gradient chunk).
 #include "moe_internal.h"
 #include "moe_ep.h"
 
@@ -647,7 +653,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
     float wt = 0.0f;
     if (lane < k) {
         p = a.pos[(int64_t)t * k + lane];
-        wt = a.w[(int64_t)t * k + lane];
+        wt = a.w != nullptr ? a.w[(int64_t)t * k + lane] : 1.0f;   // no weights: dispatch backward
         if (p < -1 || p >= a.rows_cap) {
             atomicOr(a.err, kErrBounds);
             p = -1;
@@ -699,6 +705,127 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
     }
 }
 
+// ============================================================== combine backward
+// Sum over the 64 lanes; every lane gets the total (fixed butterfly order).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// One wavefront per (token, row slice), like k_combine.  For each 16-byte chunk
+// of the token's output gradient: load it and the k routed expert-output rows,
+// write bf16(w_j * go) to each routed row of grad_y, and accumulate the chunk's
+// products go * y_j into one fp32 partial dot product per slot (a product of
+// two bf16 values is exact in fp32, so a fused multiply-add rounds exactly as a
+// separate add would).  The slice's partials are reduced over the wavefront;
+// with one slice per token the wavefront writes grad_w directly, otherwise it
+// stores its partials, and the last slice of the token to arrive (device-scope
+// counter, reset by that wavefront) adds them in slice order -- the result
+// does not depend on which wavefront finishes last.
+template <int C, int KMAX>
+__global__ __launch_bounds__(kBlockThreads) void k_combine_bwd(CombineBwdArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w;
+    if (item >= (int64_t)a.T * a.nslices) return;
+    const int t = (int)(item / a.nslices);
+    const int s = (int)(item - (int64_t)t * a.nslices);
+    const int k = a.k;
+
+    int p = -1;
+    float wt = 0.0f;
+    if (lane < k) {
+        p = a.pos[(int64_t)t * k + lane];
+        wt = a.w[(int64_t)t * k + lane];
+        if (p < -1 || p >= a.rows_cap) {
+            atomicOr(a.err, kErrBounds);
+            p = -1;
+        }
+    }
+    int pj[KMAX];
+    float wj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        pj[j] = readlane(p, j);
+        wj[j] = readlane(wt, j);
+    }
+
+    const int64_t nchunk = a.H / 8;
+    const int64_t g0 = (int64_t)s * 64 * C + lane;
+    const u32x4* __restrict__ go = reinterpret_cast<const u32x4*>(a.go) + (int64_t)t * nchunk;
+    const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.y);
+    u32x4* __restrict__ gy = reinterpret_cast<u32x4*>(a.gy);
+    float dot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) dot[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int64_t g = g0 + i * 64;
+        const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
+        if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
+            const u32x4 gv = __builtin_nontemporal_load(go + g);
+            u32x4 v[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (pj[j] >= 0) v[j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g);
+            float gf[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
+                           bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                if (pj[j] >= 0) {
+                    float d = dot[j];
+                    d = __builtin_fmaf(gf[0], bf16_lo(v[j].x), d);
+                    d = __builtin_fmaf(gf[1], bf16_hi(v[j].x), d);
+                    d = __builtin_fmaf(gf[2], bf16_lo(v[j].y), d);
+                    d = __builtin_fmaf(gf[3], bf16_hi(v[j].y), d);
+                    d = __builtin_fmaf(gf[4], bf16_lo(v[j].z), d);
+                    d = __builtin_fmaf(gf[5], bf16_hi(v[j].z), d);
+                    d = __builtin_fmaf(gf[6], bf16_lo(v[j].w), d);
+                    d = __builtin_fmaf(gf[7], bf16_hi(v[j].w), d);
+                    dot[j] = d;
+                    const float wv = wj[j];
+                    u32x4 o;
+                    o.x = f32_to_bf16(__fmul_rn(wv, gf[0])) | (f32_to_bf16(__fmul_rn(wv, gf[1])) << 16);
+                    o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
+                    o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
+                    o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
+                    gy[(int64_t)pj[j] * nchunk + g] = o;
+                }
+            }
+        }
+    }
+
+    // lane j keeps slot j's wavefront total
+    float mine = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k && pj[j] >= 0) {
+            const float tot = wave_sum(dot[j]);
+            if (lane == j) mine = tot;
+        }
+    }
+    if (a.nslices == 1) {
+        if (lane < k) a.gw[(int64_t)t * k + lane] = mine;
+        return;
+    }
+    float* part = a.part + (int64_t)t * a.nslices * k;
+    if (lane < k) part[(int64_t)s * k + lane] = mine;
+    __threadfence();
+    uint32_t old = 0;
+    if (lane == 0) old = atomicAdd(&a.arrive[t], 1u);
+    old = (uint32_t)readlane((int)old, 0);
+    if (old != (uint32_t)a.nslices - 1) return;
+    __threadfence();
+    if (lane < k) {
+        float acc = 0.0f;
+        for (int q = 0; q < a.nslices; ++q)
+            acc += __hip_atomic_load(&part[(int64_t)q * k + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.gw[(int64_t)t * k + lane] = acc;
+    }
+    if (lane == 0) a.arrive[t] = 0u;
+}
+
 template <int C>
 hipError_t pack_c(const PackArgs& a, bool fp8, bool ll, bool send, dim3 grid, hipStream_t st) {
     if (!fp8 && !ll && send) hipLaunchKernelGGL((k_pack<C, false, false, true>), grid, dim3(kBlockThreads), 0, st, a);
@@ -715,6 +842,14 @@ hipError_t combine_c(const CombineArgs& a, int kmax, dim3 grid, hipStream_t st) 
     if (kmax <= 8) hipLaunchKernelGGL((k_combine<C, 8>), grid, dim3(kBlockThreads), 0, st, a);
     else if (kmax <= 16) hipLaunchKernelGGL((k_combine<C, 16>), grid, dim3(kBlockThreads), 0, st, a);
     else hipLaunchKernelGGL((k_combine<C, 32>), grid, dim3(kBlockThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, dim3 grid, hipStream_t st) {
+    if (kmax <= 8) hipLaunchKernelGGL((k_combine_bwd<C, 8>), grid, dim3(kBlockThreads), 0, st, a);
+    else if (kmax <= 16) hipLaunchKernelGGL((k_combine_bwd<C, 16>), grid, dim3(kBlockThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_combine_bwd<C, 32>), grid, dim3(kBlockThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -772,6 +907,18 @@ hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_
         case 4: return combine_c<4>(a, kmax, grid, s);
         case 8: return combine_c<8>(a, kmax, grid, s);
         case 16: return combine_c<16>(a, kmax, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, hipStream_t s) {
+    const dim3 grid = items_grid((int64_t)a.T * a.nslices);
+    switch (chunks) {
+        case 1: return combine_bwd_c<1>(a, kmax, grid, s);
+        case 2: return combine_bwd_c<2>(a, kmax, grid, s);
+        case 4: return combine_bwd_c<4>(a, kmax, grid, s);
+        case 8: return combine_bwd_c<8>(a, kmax, grid, s);
+        case 16: return combine_bwd_c<16>(a, kmax, grid, s);
         default: return hipErrorInvalidValue;
     }
 }

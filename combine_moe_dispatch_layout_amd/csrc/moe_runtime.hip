@@ -71,7 +71,7 @@ moe_status check_config(const moe_config* c, Geometry* g) {
 // Workspace layout (device, one allocation, 256-byte aligned pieces).
 struct Workspace {
     size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
-        off_erank, off_srank, total;
+        off_erank, off_srank, off_bw_part, off_bw_arrive, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -92,6 +92,10 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
     w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
+    // combine backward: per-slice partial dot products and per-token arrival counters
+    const size_t max_slices = ((size_t)c->hidden / 8 + 63) / 64;
+    w.off_bw_part = take(4 * (size_t)c->max_tokens * max_slices * c->topk);
+    w.off_bw_arrive = take(4 * (size_t)c->max_tokens);
     w.total = o;
     return w;
 }
@@ -473,6 +477,76 @@ MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_dispatch_backward(moe_ctx* ctx, const void* grad_recv, const moe_handle* handle,
+                                         void* grad_x, void* stream) {
+    if (ctx == nullptr || handle == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (handle->tag != ctx->tag || handle->num_tokens < 0 || handle->num_tokens > c.max_tokens ||
+        handle->pos == nullptr)
+        return MOE_ERR_HANDLE;
+    const int32_t T = handle->num_tokens;
+    if (T == 0) return MOE_OK;
+    if (grad_recv == nullptr || grad_x == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(grad_recv) || !aligned16(grad_x)) return MOE_ERR_INVALID_ARG;
+    // the adjoint of the copy into the receive rows: combine with unit weights
+    CombineArgs a;
+    a.y = static_cast<const uint16_t*>(grad_recv);
+    a.w = nullptr;
+    a.pos = handle->pos;
+    a.out = static_cast<uint16_t*>(grad_x);
+    a.T = T;
+    a.k = c.topk;
+    a.H = c.hidden;
+    a.rows_cap = ctx->g.recv_rows;
+    a.err = ctx->err();
+    int chunks, nslices;
+    row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
+    a.nslices = nslices;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH_BWD);
+    hipError_t e = launch_combine(a, chunks, c.topk, s);
+    tl.done();
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float* topk_weights,
+                                        const void* expert_out, const moe_handle* handle,
+                                        void* grad_expert_out, float* grad_weights, void* stream) {
+    if (ctx == nullptr || handle == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (handle->tag != ctx->tag || handle->num_tokens < 0 || handle->num_tokens > c.max_tokens ||
+        handle->pos == nullptr)
+        return MOE_ERR_HANDLE;
+    const int32_t T = handle->num_tokens;
+    if (T == 0) return MOE_OK;
+    if (grad_out == nullptr || topk_weights == nullptr || expert_out == nullptr || grad_expert_out == nullptr ||
+        grad_weights == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(grad_out) || !aligned16(expert_out) || !aligned16(grad_expert_out)) return MOE_ERR_INVALID_ARG;
+    CombineBwdArgs a;
+    a.go = static_cast<const uint16_t*>(grad_out);
+    a.w = topk_weights;
+    a.y = static_cast<const uint16_t*>(expert_out);
+    a.pos = handle->pos;
+    a.gy = static_cast<uint16_t*>(grad_expert_out);
+    a.gw = grad_weights;
+    a.part = reinterpret_cast<float*>(ctx->ws + ctx->wl.off_bw_part);
+    a.arrive = reinterpret_cast<uint32_t*>(ctx->ws + ctx->wl.off_bw_arrive);
+    a.T = T;
+    a.k = c.topk;
+    a.H = c.hidden;
+    a.rows_cap = ctx->g.recv_rows;
+    a.err = ctx->err();
+    int chunks, nslices;
+    row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
+    a.nslices = nslices;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE_BWD);
+    hipError_t e = launch_combine_bwd(a, chunks, c.topk, s);
+    tl.done();
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags) {
     if (ctx == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -506,8 +580,8 @@ MOE_API moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches) {
 MOE_API moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches) {
     if (ctx == nullptr || !ctx->timing) return MOE_ERR_INVALID_ARG;
     moe_status st = MOE_OK;
-    double tot[MOE_KERNEL_COUNT] = {0, 0, 0};
-    int64_t cnt[MOE_KERNEL_COUNT] = {0, 0, 0};
+    double tot[MOE_KERNEL_COUNT] = {};
+    int64_t cnt[MOE_KERNEL_COUNT] = {};
     for (size_t i = 0; i < ctx->kid.size(); ++i) {
         float ms = 0.f;
         if (hipEventSynchronize(ctx->ev1[i]) != hipSuccess ||

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 1
+#define MOE_EP_ABI_VERSION 2
 
 /* ---------------------------------------------------------------- status */
 typedef enum moe_status {
@@ -238,6 +238,44 @@ moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, in
 moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float* topk_weights,
                        const moe_handle* handle, void* out, void* stream);
 
+/* ---------------------------------------------------------------- backward */
+/* Gradients of dispatch and combine for training (DeepTech release article,
+ * feature list: the high-throughput kernels serve training).  The pages give
+ * no formulas; these are the derivatives of the forward definitions above,
+ * with the bf16 roundings and the FP8 quantisation passed through as the
+ * identity.  Gradients are bf16 in every quant mode.  Both calls read the
+ * routing from a handle of the last moe_dispatch (same checks as moe_combine)
+ * and return MOE_OK at once when it holds no tokens.
+ *
+ * moe_dispatch_backward: the adjoint of dispatch's copy into the receive rows.
+ *   grad_recv  bf16 rows in the receive layout of the handle (row pos[t, j]
+ *              holds the gradient of the copy of token t for slot j)
+ *   grad_x     bf16 [num_tokens, H] output
+ * grad_x[t, h] = bf16_rne( sum over valid j, ascending, of grad_recv[pos[t, j], h] ),
+ * accumulated in fp32 from +0 (combine with every weight 1; a token with no
+ * valid slot gets +0).  Send rows carry no gradient of their own: in a
+ * multi-GPU exchange they are the transport of the receive rows. */
+moe_status moe_dispatch_backward(moe_ctx* ctx, const void* grad_recv, const moe_handle* handle,
+                                 void* grad_x, void* stream);
+
+/* moe_combine_backward: gradients of combine with respect to the expert outputs
+ * and the weights.
+ *   grad_out         bf16 [num_tokens, H] gradient of combine's output
+ *   topk_weights     fp32 [num_tokens, k], as passed to moe_combine
+ *   expert_out       bf16 rows in the receive layout, as passed to moe_combine
+ *   grad_expert_out  bf16 output rows in the receive layout: for each valid
+ *                    slot, row pos[t, j] = bf16_rne(w[t, j] * grad_out[t])
+ *                    (fp32 product, then one rounding); rows no slot points
+ *                    at are not written
+ *   grad_weights     fp32 [num_tokens, k] output: the dot product of
+ *                    grad_out[t] with expert_out[pos[t, j]] (fp32 sums of the
+ *                    exact bf16 products, in a fixed order; 0 for an empty slot)
+ * Uses a context workspace for the per-slice partial dot products: calls on
+ * one context must not overlap. */
+moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float* topk_weights,
+                                const void* expert_out, const moe_handle* handle,
+                                void* grad_expert_out, float* grad_weights, void* stream);
+
 /* ---------------------------------------------------------------- errors */
 /* Synchronize `stream`, read and clear the sticky device error word.
  * Returns MOE_OK, MOE_ERR_BAD_TOPK or MOE_ERR_DEVICE_BOUNDS (the first set,
@@ -255,7 +293,9 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_LAYOUT = 0,   /* count + scan */
     MOE_KERNEL_DISPATCH = 1, /* pack / permute / quantise */
     MOE_KERNEL_COMBINE = 2,  /* gather-reduce */
-    MOE_KERNEL_COUNT = 3
+    MOE_KERNEL_DISPATCH_BWD = 3,  /* dispatch backward (gather-sum) */
+    MOE_KERNEL_COMBINE_BWD = 4,   /* combine backward (weighted scatter + dot products) */
+    MOE_KERNEL_COUNT = 5
 } moe_kernel_id;
 
 moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches);

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) >= 12
+    assert len(names) >= 14
     assert set(names) == set(moe.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -118,6 +118,8 @@ def test_null_arguments_rejected(lib):
     assert lib.moe_dispatch_layout(None, None, 0, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(None, None, None, 0, 0, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(None, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(None, None, None, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_poll_error(None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_begin(None, 4) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_end(None, None, None) == moe.MOE_ERR_INVALID_ARG
