@@ -1,7 +1,10 @@
 """Benchmark: MoE dispatch layout + dispatch + combine on one MI355X.
 
 One step = the whole hot path over one batch: moe_dispatch_layout, then
-moe_dispatch reusing that layout, then moe_combine of the expert outputs.
+moe_dispatch reusing that layout, then moe_combine of the expert outputs
+(low-latency workloads: moe_dispatch straight from topk_idx, then
+moe_combine).  Side measurements: the 128-token decode step, and the backward
+step (moe_dispatch_backward + moe_combine_backward) of the main workload.
 Default workload: prefill, 4096 tokens x hidden 7168, 256 experts over 32
 virtual ranks, top-8, bf16 dispatch into per-rank send buffers and the
 expert-major receive layout, bf16 combine.  Inputs are resident in HBM before
@@ -37,6 +40,10 @@ def parse():
                    choices=["tiny", "decode", "prefill", "grouped", "skewed"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="skip the 128-token decode side measurement")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward side measurement")
+    p.add_argument("--step", default="forward", choices=["forward", "backward"],
+                   help="which step the main line times: forward (layout + dispatch + combine) or "
+                        "backward (dispatch backward + combine backward)")
     p.add_argument("--cpu-reps", type=int, default=3)
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + steps only (for rocprofv3), print the JSON line without baselines")
@@ -60,6 +67,50 @@ def algorithmic_bytes(c, T, n_send, n_pairs, n_slots):
                     + 4 * (2 * E + R + 2))
     combine = 2 * n_pairs * H + 8 * n_slots + 2 * T * H
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def backward_bytes(c, T, n_pairs):
+    """Algorithmic bytes of the backward kernels: dispatch backward reads the
+    routed gradient rows and writes one row per token; combine backward reads
+    the output gradient and the routed expert outputs and writes the routed
+    gradient rows and grad_w (plus pos and weights per slot)."""
+    H, k = c["H"], c["k"]
+    return {"dispatch_bwd": 2 * n_pairs * H + 4 * T * k + 2 * T * H,
+            "combine_bwd": 2 * T * H + 8 * T * k + 4 * n_pairs * H + 4 * T * k}
+
+
+def setup_backward(torch, s):
+    """Gradient buffers of the backward step, drawn on the GPU (seeded)."""
+    c, y = s["c"], s["y"]
+    dev = y.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242 + c["index"])
+    s["grad_recv"] = torch.randn(y.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    s["grad_out"] = torch.randn((c["T"], c["H"]), generator=g, device=dev,
+                                dtype=torch.float32).to(torch.bfloat16)
+    s["grad_x"] = torch.empty((c["T"], c["H"]), dtype=torch.bfloat16, device=dev)
+    s["grad_y"] = torch.empty_like(y)
+    s["grad_w"] = torch.empty((c["T"], c["k"]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+
+def step_bwd(moe, s):
+    """Backward of one step: dispatch backward (gradient rows -> tokens), then
+    combine backward (output gradient -> expert-output gradient rows and grad_w)."""
+    moe.moe_dispatch_backward(s["ctx"], s["grad_recv"], s["h"], grad_x=s["grad_x"])
+    moe.moe_combine_backward(s["ctx"], s["grad_out"], s["w"], s["y"], s["h"],
+                             grad_expert_out=s["grad_y"], grad_weights=s["grad_w"])
+
+
+def kernel_table(kt, alg):
+    out = {}
+    for name, b in alg.items():
+        n = kt[name]["launches"]
+        if n == 0 or b == 0:
+            continue
+        us = 1e3 * kt[name]["total_ms"] / n
+        out[name] = {"us": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def setup(moe, W, torch, name, T=None):
@@ -191,24 +242,25 @@ def main():
     s = setup(moe, W, torch, a.workload)
     c = s["c"]
     T = c["T"]
-    alg = algorithmic_bytes(c, T, s["n_send"], s["n_pairs"], T * c["k"])
-    fn = step_ll if c["layout"] == 1 else step
-    if fn is step_ll:
-        alg["layout"] = 0                     # the routing is read inside the fused dispatch
+    if a.step == "backward":
+        setup_backward(torch, s)
+        alg = backward_bytes(c, T, s["n_pairs"])
+        fn = step_bwd
+        step_desc = "dispatch backward + combine backward"
+    else:
+        alg = algorithmic_bytes(c, T, s["n_send"], s["n_pairs"], T * c["k"])
+        fn = step_ll if c["layout"] == 1 else step
+        if fn is step_ll:
+            alg["layout"] = 0                     # the routing is read inside the fused dispatch
+        step_desc = ("dispatch from topk_idx (fused) + combine" if fn is step_ll
+                     else "layout + dispatch(reuse layout) + combine")
     step_bytes = sum(alg.values())
     wall = timed(moe, torch, s, a.steps, a.warmup, fn=fn)
     kt = timed_kernels(moe, torch, s, a.steps, fn=fn)
     ms_per_step = 1e3 * wall / a.steps
     value = step_bytes / (wall / a.steps) / 1e9
 
-    per_kernel = {}
-    for name in ("layout", "dispatch", "combine"):
-        n = kt[name]["launches"]
-        if n == 0:
-            continue
-        us = 1e3 * kt[name]["total_ms"] / n
-        per_kernel[name] = {"us": round(us, 2), "alg_bytes": alg[name],
-                            "GB/s": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+    per_kernel = kernel_table(kt, alg)
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     achieved = per_kernel[dom]["GB/s"]
 
@@ -228,8 +280,7 @@ def main():
         "config": {"workload": "%s: T=%d H=%d E=%d R=%d top-%d %s %s" % (
             a.workload, T, c["H"], c["E"], c["R"], c["k"], "fp8" if c["quant"] else "bf16",
             "padded-LL" if c["layout"] else "send+contiguous"),
-            "step": "dispatch from topk_idx (fused) + combine" if fn is step_ll
-                    else "layout + dispatch(reuse layout) + combine",
+            "step": step_desc,
             "alg_bytes_per_step": step_bytes, "n_send_rows": s["n_send"], "n_recv_rows": s["n_pairs"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
         "kernels": per_kernel,
@@ -237,6 +288,23 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(dom, a.workload)},
     }
+
+    if not a.profile_only and not a.no_backward and a.step == "forward":
+        setup_backward(torch, s)
+        alg_b = backward_bytes(c, T, s["n_pairs"])
+        wall_b = timed(moe, torch, s, a.steps, a.warmup, fn=step_bwd)
+        kt_b = timed_kernels(moe, torch, s, a.steps, fn=step_bwd)
+        us_b = 1e6 * wall_b / a.steps
+        line["backward"] = {
+            "workload": line["config"]["workload"],
+            "step": "dispatch backward + combine backward",
+            "us_per_step": round(us_b, 2),
+            "alg_bytes_per_step": sum(alg_b.values()),
+            "GB/s": round(sum(alg_b.values()) / (us_b * 1e-6) / 1e9, 1),
+            "kernels": kernel_table(kt_b, alg_b)}
+        for key in ("grad_recv", "grad_out", "grad_x", "grad_y", "grad_w"):
+            del s[key]
+        torch.cuda.empty_cache()
 
     if not a.profile_only and not a.no_decode and a.workload != "decode":
         sd = setup(moe, W, torch, "decode")
@@ -258,7 +326,7 @@ def main():
         del sd, flush
         torch.cuda.empty_cache()
 
-    if not a.profile_only and not a.no_cpu_baseline:
+    if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
         sec, _ = cpu_baseline(s, a.cpu_reps)
         line["cpu_baseline"] = {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle",

@@ -17,6 +17,10 @@ constexpr int kWavesPerBlock = kBlockThreads / 64;
 constexpr int kFusedMaxEntries = 2048;
 constexpr int kFusedMaxTokens = 512;
 
+// Combine backward: one block per token, one wavefront per row slice, at most
+// this many wavefronts (fewer above eight slots, which need more registers).
+constexpr int bwd_max_waves(int k) { return k > 8 ? 4 : 16; }
+
 // Bits of the sticky device error word.
 constexpr uint32_t kErrBadTopk = 1u;
 constexpr uint32_t kErrBounds = 2u;
@@ -93,10 +97,8 @@ struct CombineBwdArgs {
     const int32_t* pos;        // [T, k]
     uint16_t* gy;              // bf16 gradient of the expert outputs (rows at pos)
     float* gw;                 // [T, k] gradient of the weights
-    float* part;               // [T, nslices, k] partial dot products (nslices > 1)
-    uint32_t* arrive;          // [T] arrival counters, zero between launches
     int32_t T, k, H;
-    int32_t nslices;
+    int32_t nslices;           // wavefronts per block (one block per token), <= bwd_max_waves(k)
     int64_t rows_cap;
     uint32_t* err;
 };

@@ -713,24 +713,24 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// One wavefront per (token, row slice), like k_combine.  For each 16-byte chunk
-// of the token's output gradient: load it and the k routed expert-output rows,
-// write bf16(w_j * go) to each routed row of grad_y, and accumulate the chunk's
-// products go * y_j into one fp32 partial dot product per slot (a product of
-// two bf16 values is exact in fp32, so a fused multiply-add rounds exactly as a
-// separate add would).  The slice's partials are reduced over the wavefront;
-// with one slice per token the wavefront writes grad_w directly, otherwise it
-// stores its partials, and the last slice of the token to arrive (device-scope
-// counter, reset by that wavefront) adds them in slice order -- the result
-// does not depend on which wavefront finishes last.
+// One block per token, one wavefront per row slice (blockDim.x / 64 slices of
+// C 16-byte chunks per lane).  For each chunk of the token's output gradient:
+// load it and the routed expert-output rows (eight slots at a time, to bound
+// registers), write bf16(w_j * go) to each routed row of grad_y, and
+// accumulate the chunk's products go * y_j into one fp32 partial dot product
+// per slot (a product of two bf16 values is exact in fp32, so a fused
+// multiply-add rounds exactly as a separate add would).  Partials are reduced
+// over the wavefront (fixed butterfly), then over the block's wavefronts in
+// wavefront order through LDS: deterministic, and no device-scope fence (on
+// this chip a release fence writes back the L2, which costs more than the
+// whole kernel when every wavefront issues one).
 template <int C, int KMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_combine_bwd(CombineBwdArgs a) {
+__global__ __launch_bounds__(64 * bwd_max_waves(KMAX)) void k_combine_bwd(CombineBwdArgs a) {
+    __shared__ float red[bwd_max_waves(KMAX)][KMAX];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w;
-    if (item >= (int64_t)a.T * a.nslices) return;
-    const int t = (int)(item / a.nslices);
-    const int s = (int)(item - (int64_t)t * a.nslices);
+    const int s = __builtin_amdgcn_readfirstlane(tid >> 6);   // slice = wavefront
+    const int nw = blockDim.x >> 6;
+    const int t = blockIdx.x;
     const int k = a.k;
 
     int p = -1;
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine_bwd(CombineBwdArgs a)
         p = a.pos[(int64_t)t * k + lane];
         wt = a.w[(int64_t)t * k + lane];
         if (p < -1 || p >= a.rows_cap) {
-            atomicOr(a.err, kErrBounds);
+            if (s == 0) atomicOr(a.err, kErrBounds);
             p = -1;
         }
     }
@@ -765,65 +765,58 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine_bwd(CombineBwdArgs a)
         const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
         if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
             const u32x4 gv = __builtin_nontemporal_load(go + g);
-            u32x4 v[KMAX];
+            const float gf[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
+                                 bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j)
-                if (pj[j] >= 0) v[j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g);
-            float gf[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
-                           bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+            for (int jb = 0; jb < KMAX; jb += 8) {
+                if (jb >= k) break;
+                u32x4 v[8];
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) {
-                if (pj[j] >= 0) {
-                    float d = dot[j];
-                    d = __builtin_fmaf(gf[0], bf16_lo(v[j].x), d);
-                    d = __builtin_fmaf(gf[1], bf16_hi(v[j].x), d);
-                    d = __builtin_fmaf(gf[2], bf16_lo(v[j].y), d);
-                    d = __builtin_fmaf(gf[3], bf16_hi(v[j].y), d);
-                    d = __builtin_fmaf(gf[4], bf16_lo(v[j].z), d);
-                    d = __builtin_fmaf(gf[5], bf16_hi(v[j].z), d);
-                    d = __builtin_fmaf(gf[6], bf16_lo(v[j].w), d);
-                    d = __builtin_fmaf(gf[7], bf16_hi(v[j].w), d);
-                    dot[j] = d;
-                    const float wv = wj[j];
-                    u32x4 o;
-                    o.x = f32_to_bf16(__fmul_rn(wv, gf[0])) | (f32_to_bf16(__fmul_rn(wv, gf[1])) << 16);
-                    o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
-                    o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
-                    o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
-                    gy[(int64_t)pj[j] * nchunk + g] = o;
+                for (int jj = 0; jj < 8; ++jj)
+                    if (pj[jb + jj] >= 0) v[jj] = __builtin_nontemporal_load(y + (int64_t)pj[jb + jj] * nchunk + g);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int j = jb + jj;
+                    if (pj[j] >= 0) {
+                        float d = dot[j];
+                        d = __builtin_fmaf(gf[0], bf16_lo(v[jj].x), d);
+                        d = __builtin_fmaf(gf[1], bf16_hi(v[jj].x), d);
+                        d = __builtin_fmaf(gf[2], bf16_lo(v[jj].y), d);
+                        d = __builtin_fmaf(gf[3], bf16_hi(v[jj].y), d);
+                        d = __builtin_fmaf(gf[4], bf16_lo(v[jj].z), d);
+                        d = __builtin_fmaf(gf[5], bf16_hi(v[jj].z), d);
+                        d = __builtin_fmaf(gf[6], bf16_lo(v[jj].w), d);
+                        d = __builtin_fmaf(gf[7], bf16_hi(v[jj].w), d);
+                        dot[j] = d;
+                        const float wv = wj[j];
+                        u32x4 o;
+                        o.x = f32_to_bf16(__fmul_rn(wv, gf[0])) | (f32_to_bf16(__fmul_rn(wv, gf[1])) << 16);
+                        o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
+                        o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
+                        o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
+                        gy[(int64_t)pj[j] * nchunk + g] = o;
+                    }
                 }
             }
         }
     }
 
-    // lane j keeps slot j's wavefront total
-    float mine = 0.0f;
+    // wavefront totals -> LDS (lane j holds slot j), then wavefront 0 adds the
+    // slices in order
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (j < k && pj[j] >= 0) {
             const float tot = wave_sum(dot[j]);
-            if (lane == j) mine = tot;
+            if (lane == 0) red[s][j] = tot;
         }
     }
-    if (a.nslices == 1) {
-        if (lane < k) a.gw[(int64_t)t * k + lane] = mine;
-        return;
-    }
-    float* part = a.part + (int64_t)t * a.nslices * k;
-    if (lane < k) part[(int64_t)s * k + lane] = mine;
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(&a.arrive[t], 1u);
-    old = (uint32_t)readlane((int)old, 0);
-    if (old != (uint32_t)a.nslices - 1) return;
-    __threadfence();
-    if (lane < k) {
+    __syncthreads();
+    if (s == 0 && lane < k) {
         float acc = 0.0f;
-        for (int q = 0; q < a.nslices; ++q)
-            acc += __hip_atomic_load(&part[(int64_t)q * k + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p >= 0)
+            for (int q = 0; q < nw; ++q) acc += red[q][lane];
         a.gw[(int64_t)t * k + lane] = acc;
     }
-    if (lane == 0) a.arrive[t] = 0u;
 }
 
 template <int C>
@@ -846,10 +839,11 @@ hipError_t combine_c(const CombineArgs& a, int kmax, dim3 grid, hipStream_t st) 
 }
 
 template <int C>
-hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, dim3 grid, hipStream_t st) {
-    if (kmax <= 8) hipLaunchKernelGGL((k_combine_bwd<C, 8>), grid, dim3(kBlockThreads), 0, st, a);
-    else if (kmax <= 16) hipLaunchKernelGGL((k_combine_bwd<C, 16>), grid, dim3(kBlockThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_combine_bwd<C, 32>), grid, dim3(kBlockThreads), 0, st, a);
+hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, hipStream_t st) {
+    const dim3 grid((unsigned)a.T), block((unsigned)(64 * waves));
+    if (kmax <= 8) hipLaunchKernelGGL((k_combine_bwd<C, 8>), grid, block, 0, st, a);
+    else if (kmax <= 16) hipLaunchKernelGGL((k_combine_bwd<C, 16>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_combine_bwd<C, 32>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -912,13 +906,14 @@ hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_
 }
 
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, hipStream_t s) {
-    const dim3 grid = items_grid((int64_t)a.T * a.nslices);
+    // one block per token, one wavefront per slice
+    if (a.T < 1 || a.nslices < 1 || a.nslices > bwd_max_waves(kmax)) return hipErrorInvalidValue;
     switch (chunks) {
-        case 1: return combine_bwd_c<1>(a, kmax, grid, s);
-        case 2: return combine_bwd_c<2>(a, kmax, grid, s);
-        case 4: return combine_bwd_c<4>(a, kmax, grid, s);
-        case 8: return combine_bwd_c<8>(a, kmax, grid, s);
-        case 16: return combine_bwd_c<16>(a, kmax, grid, s);
+        case 1: return combine_bwd_c<1>(a, kmax, a.nslices, s);
+        case 2: return combine_bwd_c<2>(a, kmax, a.nslices, s);
+        case 4: return combine_bwd_c<4>(a, kmax, a.nslices, s);
+        case 8: return combine_bwd_c<8>(a, kmax, a.nslices, s);
+        case 16: return combine_bwd_c<16>(a, kmax, a.nslices, s);
         default: return hipErrorInvalidValue;
     }
 }

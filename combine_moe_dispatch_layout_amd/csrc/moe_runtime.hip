@@ -71,7 +71,7 @@ moe_status check_config(const moe_config* c, Geometry* g) {
 // Workspace layout (device, one allocation, 256-byte aligned pieces).
 struct Workspace {
     size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
-        off_erank, off_srank, off_bw_part, off_bw_arrive, total;
+        off_erank, off_srank, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -92,10 +92,6 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
     w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
-    // combine backward: per-slice partial dot products and per-token arrival counters
-    const size_t max_slices = ((size_t)c->hidden / 8 + 63) / 64;
-    w.off_bw_part = take(4 * (size_t)c->max_tokens * max_slices * c->topk);
-    w.off_bw_arrive = take(4 * (size_t)c->max_tokens);
     w.total = o;
     return w;
 }
@@ -530,15 +526,19 @@ MOE_API moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, cons
     a.pos = handle->pos;
     a.gy = static_cast<uint16_t*>(grad_expert_out);
     a.gw = grad_weights;
-    a.part = reinterpret_cast<float*>(ctx->ws + ctx->wl.off_bw_part);
-    a.arrive = reinterpret_cast<uint32_t*>(ctx->ws + ctx->wl.off_bw_arrive);
     a.T = T;
     a.k = c.topk;
     a.H = c.hidden;
     a.rows_cap = ctx->g.recv_rows;
     a.err = ctx->err();
+    // one block per token with one wavefront per slice: widen the slices until
+    // they fit in one block
     int chunks, nslices;
     row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
+    while (nslices > bwd_max_waves(c.topk)) {
+        chunks *= 2;
+        nslices = (int)((c.hidden / 8 + 64 * chunks - 1) / (64 * chunks));
+    }
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE_BWD);

@@ -269,9 +269,7 @@ moe_status moe_dispatch_backward(moe_ctx* ctx, const void* grad_recv, const moe_
  *                    at are not written
  *   grad_weights     fp32 [num_tokens, k] output: the dot product of
  *                    grad_out[t] with expert_out[pos[t, j]] (fp32 sums of the
- *                    exact bf16 products, in a fixed order; 0 for an empty slot)
- * Uses a context workspace for the per-slice partial dot products: calls on
- * one context must not overlap. */
+ *                    exact bf16 products, in a fixed order; 0 for an empty slot) */
 moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float* topk_weights,
                                 const void* expert_out, const moe_handle* handle,
                                 void* grad_expert_out, float* grad_weights, void* stream);

@@ -197,8 +197,8 @@ def test_backward_hidden_sizes(gpu, H):
 
 @pytest.mark.parametrize("chunks", [1, 2, 4, 8, 16])
 def test_backward_row_split(gpu, chunks):
-    """Every slice width: 14 slices per 7168-wide row at 1 chunk per lane down
-    to a single slice at 16 (grad_w written directly)."""
+    """Every slice width: 14 wavefronts per token (7168-wide rows, 1 chunk per
+    lane) down to a single wavefront at 16 chunks per lane."""
     c = small_cfg("prefill", H=7168)
     d = W.make("prefill", T=200)
     c["max_tokens"] = 200
@@ -206,15 +206,18 @@ def test_backward_row_split(gpu, chunks):
                  tag="chunks%d" % chunks, repeat=2)
 
 
-@pytest.mark.parametrize("T,k", [(300, 1), (64, 32), (65, 17)])
-def test_backward_topk_extremes(gpu, T, k):
-    c = dict(index=11, T=T, H=1024, E=64, R=8, k=k, quant=W.QUANT_BF16,
+@pytest.mark.parametrize("T,k,H", [(300, 1, 1024), (64, 32, 1024), (65, 17, 1024), (64, 32, 7168),
+                                   (33, 17, 32768), (40, 9, 7168)])
+def test_backward_topk_extremes(gpu, T, k, H):
+    """k = 1 up to 32 (above 8 slots a token gets at most 4 wavefronts, so the
+    slices are wide)."""
+    c = dict(index=11, T=T, H=H, E=64, R=8, k=k, quant=W.QUANT_BF16,
              layout=W.LAYOUT_CONTIGUOUS, max_tokens=T)
     rng = np.random.Generator(np.random.PCG64(T + 31 * k))
     idx = W.route_uniform(rng, T, c["E"], k)
     x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
-    run_backward(gpu, c, x, idx, w, max_tokens=T, tag="k%d" % k)
+    run_backward(gpu, c, x, idx, w, max_tokens=T, tag="k%d-H%d" % (k, H))
 
 
 @pytest.mark.parametrize("name", ["prefill", "decode"])
@@ -230,12 +233,12 @@ def test_backward_empty_slots(gpu, name):
 
 
 def test_backward_consecutive_calls_shrinking(gpu):
-    """The arrival counters of combine backward are left at zero: a second call
-    with fewer tokens on the same context still matches the oracle."""
+    """Two calls in a row on one context, the second with fewer tokens: nothing
+    carries over from the first."""
     c = small_cfg("prefill", H=7168)
     d = W.make("prefill", T=300)
     ctx = gpu.Context(gpu.make_config(300, c["H"], c["E"], c["R"], c["k"], 0, c["quant"], c["layout"]))
-    ctx.tune(0, 1)                       # 14 slices per row: the arrival path
+    ctx.tune(0, 1)                       # 14 wavefronts per token
     bufs = gpu.DispatchBuffers(ctx)
     h = gpu.Handle(ctx)
     n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
