@@ -5,7 +5,7 @@ include/moe_ep.h); this package is its thin Python binding.  PyTorch is used
 only for device memory and streams.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, KERNEL_NAMES, LIB_PATH, Context, DispatchBuffers, Handle, MoeError,
+    EXPORTS, KERNEL_NAMES, LIB_PATH, Context, DispatchBuffers, Handle, Hook, MoeError,
     MOE_BUF_COMBINE_OUT, MOE_BUF_EXPERT_OUT, MOE_BUF_HANDLE_EXPERT_OFFSETS, MOE_BUF_HANDLE_POS,
     MOE_BUF_HANDLE_RANK_OFFSETS, MOE_BUF_HANDLE_RECV_COUNTS, MOE_BUF_HANDLE_RECV_SRC,
     MOE_BUF_HANDLE_SEND_SRC, MOE_BUF_LAYOUT_EXPERT_COUNTS, MOE_BUF_LAYOUT_RANK_COUNTS,

@@ -68,7 +68,8 @@ class moe_handle(ctypes.Structure):
 # the full list of symbols include/moe_ep.h declares
 EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy", "moe_ctx_config",
            "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_backward",
-           "moe_combine_backward", "moe_poll_error", "moe_timing_begin", "moe_timing_end")
+           "moe_combine_backward", "moe_ctx_set_max_workgroups", "moe_hook_create", "moe_hook_destroy",
+           "moe_hook_record", "moe_hook_wait", "moe_poll_error", "moe_timing_begin", "moe_timing_end")
 
 _lib = None
 
@@ -97,6 +98,11 @@ def load_library(path=LIB_PATH):
         "moe_combine": [vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp],
         "moe_dispatch_backward": [vp, vp, ctypes.POINTER(moe_handle), vp, vp],
         "moe_combine_backward": [vp, vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp, vp],
+        "moe_ctx_set_max_workgroups": [vp, i32],
+        "moe_hook_create": [ctypes.POINTER(vp)],
+        "moe_hook_destroy": [vp],
+        "moe_hook_record": [vp, vp],
+        "moe_hook_wait": [vp, vp],
         "moe_poll_error": [vp, vp, u32p],
         "moe_timing_begin": [vp, i32],
         "moe_timing_end": [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
@@ -122,8 +128,10 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream(stream=None):
+    """HIP stream handle of a torch stream (default: the current stream)."""
+    st = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(st.cuda_stream)
 
 
 def make_config(max_tokens, hidden, num_experts, num_ranks, topk, src_rank=0,
@@ -172,6 +180,10 @@ class Context:
     def tune(self, dispatch_chunks=0, combine_chunks=0):
         _check(load_library().moe_ctx_tune(self.handle, dispatch_chunks, combine_chunks), "moe_ctx_tune")
 
+    def set_max_workgroups(self, n):
+        """Cap the workgroups of the dispatch, combine and backward kernels (0 = none)."""
+        _check(load_library().moe_ctx_set_max_workgroups(self.handle, int(n)), "moe_ctx_set_max_workgroups")
+
     def timing_begin(self, max_launches):
         _check(load_library().moe_timing_begin(self.handle, max_launches), "moe_timing_begin")
 
@@ -181,6 +193,32 @@ class Context:
         cnt = (ctypes.c_int64 * n)()
         _check(load_library().moe_timing_end(self.handle, tot, cnt), "moe_timing_end")
         return {KERNEL_NAMES[i]: {"total_ms": tot[i], "launches": cnt[i]} for i in range(n)}
+
+
+class Hook:
+    """Issue/complete split: record() after enqueuing dispatch or combine on a
+    side stream, wait() on the stream that needs the results."""
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        _check(load_library().moe_hook_create(ctypes.byref(self.h)), "moe_hook_create")
+
+    def record(self, stream=None):
+        _check(load_library().moe_hook_record(self.h, _stream(stream)), "moe_hook_record")
+
+    def wait(self, stream=None):
+        _check(load_library().moe_hook_wait(self.h, _stream(stream)), "moe_hook_wait")
+
+    def close(self):
+        if self.h:
+            _check(load_library().moe_hook_destroy(self.h), "moe_hook_destroy")
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Handle:

@@ -105,10 +105,12 @@ struct CombineBwdArgs {
 
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
 hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s);
-// chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16)
-hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s);
-hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, hipStream_t s);
+// chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16).
+// max_blocks > 0 caps the grid; the kernels then loop over their work items.
+hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, int max_blocks,
+                       hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s);
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s);
 // Low-latency dispatch without a separate layout launch (T * k <= kFusedMaxEntries).
 hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t s);
 

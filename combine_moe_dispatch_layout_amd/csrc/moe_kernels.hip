@@ -387,17 +387,9 @@ __device__ __forceinline__ void quantize_slice(const u32x4* v, u32x2* q, float* 
     }
 }
 
+// One (token, row slice) work item of the dispatch, done by one wavefront.
 template <int C, bool FP8, bool LL, bool SEND>
-__global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    if (blockIdx.x == 0) {   // handle copies of the layout offsets and counts
-        for (int i = tid; i <= a.E; i += kBlockThreads) a.h_eoff[i] = a.eoff[i];
-        for (int i = tid; i < a.E; i += kBlockThreads) a.h_recv_counts[i] = a.cnt_e[i];
-        for (int i = tid; i <= a.R; i += kBlockThreads) a.h_roff[i] = a.roff[i];
-    }
-    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w;
-    if (item >= (int64_t)a.T * a.nslices) return;
+__device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int lane) {
     const int t = (int)(item / a.nslices);
     const int s = (int)(item - (int64_t)t * a.nslices);
     const int k = a.k;
@@ -492,6 +484,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
             }
         }
     }
+}
+
+// Grid-stride over the work items, so that the grid can be capped (a cap on
+// the workgroups the dispatch occupies) without changing any result.
+template <int C, bool FP8, bool LL, bool SEND>
+__global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    if (blockIdx.x == 0) {   // handle copies of the layout offsets and counts
+        for (int i = tid; i <= a.E; i += kBlockThreads) a.h_eoff[i] = a.eoff[i];
+        for (int i = tid; i < a.E; i += kBlockThreads) a.h_recv_counts[i] = a.cnt_e[i];
+        for (int i = tid; i <= a.R; i += kBlockThreads) a.h_roff[i] = a.roff[i];
+    }
+    const int64_t total = (int64_t)a.T * a.nslices;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w; item < total; item += stride)
+        pack_item<C, FP8, LL, SEND>(a, item, lane);
 }
 
 // ============================================================== fused low-latency dispatch
@@ -640,11 +649,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_ll_dispatch(PackArgs a) {
 
 // ============================================================== combine
 template <int C, int KMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w;
-    if (item >= (int64_t)a.T * a.nslices) return;
+__device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item, int lane) {
     const int t = (int)(item / a.nslices);
     const int s = (int)(item - (int64_t)t * a.nslices);
     const int k = a.k;
@@ -705,6 +710,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
     }
 }
 
+template <int C, int KMAX>
+__global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int64_t total = (int64_t)a.T * a.nslices;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w; item < total; item += stride)
+        combine_item<C, KMAX>(a, item, lane);
+}
+
 // ============================================================== combine backward
 // Sum over the 64 lanes; every lane gets the total (fixed butterfly order).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -723,14 +738,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 // over the wavefront (fixed butterfly), then over the block's wavefronts in
 // wavefront order through LDS: deterministic, and no device-scope fence (on
 // this chip a release fence writes back the L2, which costs more than the
-// whole kernel when every wavefront issues one).
+// whole kernel when every wavefront issues one).  Measured on MI355X:
+// non-temporal loads and stores, ~3% ahead of cached ones; the time does not
+// depend on the slice width.
 template <int C, int KMAX>
-__global__ __launch_bounds__(64 * bwd_max_waves(KMAX)) void k_combine_bwd(CombineBwdArgs a) {
-    __shared__ float red[bwd_max_waves(KMAX)][KMAX];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int s = __builtin_amdgcn_readfirstlane(tid >> 6);   // slice = wavefront
+__device__ __forceinline__ void combine_bwd_token(const CombineBwdArgs& a, int t, int s, int lane,
+                                                  float (*red)[KMAX]) {
     const int nw = blockDim.x >> 6;
-    const int t = blockIdx.x;
     const int k = a.k;
 
     int p = -1;
@@ -794,7 +808,7 @@ __global__ __launch_bounds__(64 * bwd_max_waves(KMAX)) void k_combine_bwd(Combin
                         o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
                         o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
                         o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
-                        gy[(int64_t)pj[j] * nchunk + g] = o;
+                        __builtin_nontemporal_store(o, gy + (int64_t)pj[j] * nchunk + g);
                     }
                 }
             }
@@ -817,6 +831,17 @@ __global__ __launch_bounds__(64 * bwd_max_waves(KMAX)) void k_combine_bwd(Combin
             for (int q = 0; q < nw; ++q) acc += red[q][lane];
         a.gw[(int64_t)t * k + lane] = acc;
     }
+    __syncthreads();   // red is reused by the block's next token
+}
+
+// One block per token; with a capped grid each block takes every
+// gridDim.x-th token.
+template <int C, int KMAX>
+__global__ __launch_bounds__(64 * bwd_max_waves(KMAX)) void k_combine_bwd(CombineBwdArgs a) {
+    __shared__ float red[bwd_max_waves(KMAX)][KMAX];
+    const int lane = threadIdx.x & 63;
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // slice = wavefront
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) combine_bwd_token<C, KMAX>(a, t, s, lane, red);
 }
 
 template <int C>
@@ -839,8 +864,9 @@ hipError_t combine_c(const CombineArgs& a, int kmax, dim3 grid, hipStream_t st) 
 }
 
 template <int C>
-hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, hipStream_t st) {
-    const dim3 grid((unsigned)a.T), block((unsigned)(64 * waves));
+hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, int max_blocks, hipStream_t st) {
+    const int blocks = max_blocks > 0 && a.T > max_blocks ? max_blocks : a.T;
+    const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves));
     if (kmax <= 8) hipLaunchKernelGGL((k_combine_bwd<C, 8>), grid, block, 0, st, a);
     else if (kmax <= 16) hipLaunchKernelGGL((k_combine_bwd<C, 16>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_combine_bwd<C, 32>), grid, block, 0, st, a);
@@ -849,8 +875,10 @@ hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, hipStream
 
 // At least one block: block 0 of the dispatch kernel also writes the handle's
 // offsets and counts, which must happen even when there are no tokens.
-dim3 items_grid(int64_t items) {
-    const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+// max_blocks > 0 caps the grid (the kernels loop over their items).
+dim3 items_grid(int64_t items, int max_blocks) {
+    int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
     return dim3((unsigned)(blocks > 0 ? blocks : 1));
 }
 
@@ -863,8 +891,9 @@ hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, hipStream_t s) {
-    const dim3 grid = items_grid((int64_t)a.T * a.nslices);
+hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, int max_blocks,
+                       hipStream_t s) {
+    const dim3 grid = items_grid((int64_t)a.T * a.nslices, max_blocks);
     switch (chunks) {
         case 1: return pack_c<1>(a, fp8, ll, send, grid, s);
         case 2: return pack_c<2>(a, fp8, ll, send, grid, s);
@@ -893,8 +922,8 @@ hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t 
 #undef MOE_LL_CASE
 }
 
-hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_t s) {
-    const dim3 grid = items_grid((int64_t)a.T * a.nslices);
+hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {
+    const dim3 grid = items_grid((int64_t)a.T * a.nslices, max_blocks);
     switch (chunks) {
         case 1: return combine_c<1>(a, kmax, grid, s);
         case 2: return combine_c<2>(a, kmax, grid, s);
@@ -905,15 +934,15 @@ hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, hipStream_
     }
 }
 
-hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, hipStream_t s) {
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {
     // one block per token, one wavefront per slice
     if (a.T < 1 || a.nslices < 1 || a.nslices > bwd_max_waves(kmax)) return hipErrorInvalidValue;
     switch (chunks) {
-        case 1: return combine_bwd_c<1>(a, kmax, a.nslices, s);
-        case 2: return combine_bwd_c<2>(a, kmax, a.nslices, s);
-        case 4: return combine_bwd_c<4>(a, kmax, a.nslices, s);
-        case 8: return combine_bwd_c<8>(a, kmax, a.nslices, s);
-        case 16: return combine_bwd_c<16>(a, kmax, a.nslices, s);
+        case 1: return combine_bwd_c<1>(a, kmax, a.nslices, max_blocks, s);
+        case 2: return combine_bwd_c<2>(a, kmax, a.nslices, max_blocks, s);
+        case 4: return combine_bwd_c<4>(a, kmax, a.nslices, max_blocks, s);
+        case 8: return combine_bwd_c<8>(a, kmax, a.nslices, max_blocks, s);
+        case 16: return combine_bwd_c<16>(a, kmax, a.nslices, max_blocks, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -142,6 +142,8 @@ struct moe_ctx {
     bool layout_valid;
     // tuning overrides (0 = heuristic)
     int pack_chunks, combine_chunks;
+    // cap on the workgroups of the high-throughput kernels (0 = none)
+    int max_blocks;
     // timing
     bool timing;
     int max_launches;
@@ -289,6 +291,7 @@ MOE_API moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out) {
     ctx->layout_valid = false;
     ctx->pack_chunks = 0;
     ctx->combine_chunks = 0;
+    ctx->max_blocks = 0;
     ctx->timing = false;
     ctx->max_launches = 0;
     if (hipMalloc(reinterpret_cast<void**>(&ctx->ws), ctx->wl.total) != hipSuccess) {
@@ -323,7 +326,7 @@ MOE_API moe_status moe_ctx_config(const moe_ctx* ctx, moe_config* out) {
 }
 
 // Tuning override for sweeps: chunks per lane of the dispatch / combine kernels
-// (0 = heuristic; else 1, 2, 4, 8 or 16).  Not in the public header.
+// (0 = heuristic; else 1, 2, 4, 8 or 16).
 MOE_API moe_status moe_ctx_tune(moe_ctx* ctx, int32_t pack_chunks, int32_t combine_chunks) {
     if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
     auto ok = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8 || v == 16; };
@@ -331,6 +334,52 @@ MOE_API moe_status moe_ctx_tune(moe_ctx* ctx, int32_t pack_chunks, int32_t combi
     ctx->pack_chunks = pack_chunks;
     ctx->combine_chunks = combine_chunks;
     return MOE_OK;
+}
+
+MOE_API moe_status moe_ctx_set_max_workgroups(moe_ctx* ctx, int32_t max_workgroups) {
+    if (ctx == nullptr || max_workgroups < 0) return MOE_ERR_INVALID_ARG;
+    ctx->max_blocks = max_workgroups;
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- hooks
+struct moe_hook {
+    hipEvent_t ev;
+    int device;
+};
+
+MOE_API moe_status moe_hook_create(moe_hook** out) {
+    if (out == nullptr) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    moe_hook* h = new (std::nothrow) moe_hook;
+    if (h == nullptr) return MOE_ERR_HIP;
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev, hipEventDisableTiming) != hipSuccess) {
+        delete h;
+        return MOE_ERR_HIP;
+    }
+    *out = h;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_hook_destroy(moe_hook* hook) {
+    if (hook == nullptr) return MOE_OK;
+    const hipError_t e = hipEventDestroy(hook->ev);
+    delete hook;
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_hook_record(moe_hook* hook, void* stream) {
+    if (hook == nullptr) return MOE_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != hook->device) return MOE_ERR_INVALID_ARG;
+    return hipEventRecord(hook->ev, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_hook_wait(const moe_hook* hook, void* stream) {
+    if (hook == nullptr) return MOE_ERR_INVALID_ARG;
+    return hipStreamWaitEvent(reinterpret_cast<hipStream_t>(stream), hook->ev, 0) == hipSuccess ? MOE_OK
+                                                                                                 : MOE_ERR_HIP;
 }
 
 MOE_API moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
@@ -431,9 +480,9 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     } else if (num_tokens == 0) {
         // grid of one block: block 0 copies the offsets, every wave exits (no items)
         a0.nslices = 1;
-        e = launch_pack(a0, 1, fp8, ll, !ll, s);
+        e = launch_pack(a0, 1, fp8, ll, !ll, ctx->max_blocks, s);
     } else {
-        e = launch_pack(a, chunks, fp8, ll, !ll, s);
+        e = launch_pack(a, chunks, fp8, ll, !ll, ctx->max_blocks, s);
     }
     tl.done();
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -468,7 +517,7 @@ MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE);
-    hipError_t e = launch_combine(a, chunks, c.topk, s);
+    hipError_t e = launch_combine(a, chunks, c.topk, ctx->max_blocks, s);
     tl.done();
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -500,7 +549,7 @@ MOE_API moe_status moe_dispatch_backward(moe_ctx* ctx, const void* grad_recv, co
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH_BWD);
-    hipError_t e = launch_combine(a, chunks, c.topk, s);
+    hipError_t e = launch_combine(a, chunks, c.topk, ctx->max_blocks, s);
     tl.done();
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -542,7 +591,7 @@ MOE_API moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, cons
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE_BWD);
-    hipError_t e = launch_combine_bwd(a, chunks, c.topk, s);
+    hipError_t e = launch_combine_bwd(a, chunks, c.topk, ctx->max_blocks, s);
     tl.done();
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -274,6 +274,34 @@ moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float*
                                 const void* expert_out, const moe_handle* handle,
                                 void* grad_expert_out, float* grad_weights, void* stream);
 
+/* ---------------------------------------------------------------- overlap */
+/* Resource control (DeepTech release article, feature list: flexible GPU
+ * resource control and SM-count control for the high-throughput kernels; the
+ * guide's resource-control section sets an SM limit).  At most
+ * `max_workgroups` workgroups (0 = no cap, the default) run the dispatch
+ * (layout-reusing or two-launch path), combine and backward kernels of this
+ * context; each workgroup then loops over more rows, so results are
+ * unchanged.  A workgroup is 256 threads (combine backward: 64 per row slice,
+ * up to 1024).  The layout kernel (a few workgroups) and the fused
+ * low-latency dispatch (the pages: low-latency kernels need no SM control)
+ * are not capped.  Capping leaves compute units to kernels on other streams,
+ * e.g. GEMMs overlapped with dispatch and combine. */
+moe_status moe_ctx_set_max_workgroups(moe_ctx* ctx, int32_t max_workgroups);
+
+/* Issue/complete split (the guide's hook-based communication-computation
+ * overlap, "Technical analysis"): enqueue dispatch or combine on a side stream,
+ * record a hook there right after it (the issue side returns at once), keep
+ * enqueuing compute on the main stream, and call moe_hook_wait on the main
+ * stream where the results are first needed (the complete side).  No kernel
+ * waits on the device in between.  A hook is a host object bound to the
+ * device current at moe_hook_create; it may be recorded again after each
+ * wait.  moe_hook_wait with a never-recorded hook returns at once. */
+typedef struct moe_hook moe_hook;
+moe_status moe_hook_create(moe_hook** out);
+moe_status moe_hook_destroy(moe_hook* hook);
+moe_status moe_hook_record(moe_hook* hook, void* stream);
+moe_status moe_hook_wait(const moe_hook* hook, void* stream);
+
 /* ---------------------------------------------------------------- errors */
 /* Synchronize `stream`, read and clear the sticky device error word.
  * Returns MOE_OK, MOE_ERR_BAD_TOPK or MOE_ERR_DEVICE_BOUNDS (the first set,

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) >= 14
+    assert len(names) >= 19
     assert set(names) == set(moe.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -120,6 +120,11 @@ def test_null_arguments_rejected(lib):
     assert lib.moe_combine(None, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine_backward(None, None, None, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_ctx_set_max_workgroups(None, 4) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_hook_create(None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_hook_destroy(None) == moe.MOE_OK
+    assert lib.moe_hook_record(None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_hook_wait(None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_poll_error(None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_begin(None, 4) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_end(None, None, None) == moe.MOE_ERR_INVALID_ARG

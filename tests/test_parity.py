@@ -56,14 +56,17 @@ def poison(bufs):
 
 
 def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, check_poison=True,
-             tag=""):
+             tag="", max_workgroups=0, side_stream=False):
     """Layout + dispatch + combine on the GPU and in the oracle; compare all."""
     T = idx.shape[0]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
     fp8 = c["quant"] == W.QUANT_FP8
-    log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d" %
-        (tag, T, c["H"], c["E"], c["R"], c["k"], c["quant"], c["layout"], reuse, src_rank))
+    log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d max_wg=%d side=%s" %
+        (tag, T, c["H"], c["E"], c["R"], c["k"], c["quant"], c["layout"], reuse, src_rank, max_workgroups,
+         side_stream))
     ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
+    if max_workgroups:
+        ctx.set_max_workgroups(max_workgroups)
     M = ctx.cfg.max_tokens
     ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"],
                           max_tokens=M if ll else 0, src_rank=src_rank, with_send=not ll)
@@ -77,8 +80,21 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
 
     # ---- layout
     cnt_e, cnt_r, in_rank = gpu.moe_dispatch_layout(ctx, idx_d)
-    # ---- dispatch
-    gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=reuse, bufs=bufs, handle=h)
+    # ---- dispatch (optionally issued on a side stream and completed by a hook)
+    if side_stream:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        hook = gpu.Hook()
+        with torch.cuda.stream(side):
+            gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=reuse, bufs=bufs, handle=h)
+        hook.record(side)
+        # unrelated work on the main stream while the dispatch runs
+        a = torch.randn((2048, 2048), device=dev(), dtype=torch.float32)
+        (a @ a).sum()
+        hook.wait()
+        hook.close()
+    else:
+        gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=reuse, bufs=bufs, handle=h)
     st, flags = gpu.moe_poll_error(ctx)
     assert st == (gpu.MOE_ERR_BAD_TOPK if ref["bad_ids"] else gpu.MOE_OK), (st, flags)
 
@@ -364,6 +380,34 @@ def test_expert_rank_extremes(gpu, E, R, k):
     x = W.to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
     run_case(gpu, c, x, idx, w, max_tokens=T, tag="extremes")
+
+
+# ---------------------------------------------------------------- resource control and hooks
+@pytest.mark.parametrize("max_wg", [1, 3, 64, 1000])
+@pytest.mark.parametrize("name", ["prefill", "grouped"])
+def test_max_workgroups_same_results(gpu, name, max_wg):
+    """A capped grid (each workgroup loops over more rows) gives the same bytes."""
+    c = small_cfg(name, H=1024)
+    d = W.make(name, T=700)
+    c["max_tokens"] = 700
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), d["topk_idx"], d["topk_weights"], max_tokens=700,
+             tag="maxwg-%s" % name, max_workgroups=max_wg)
+
+
+def test_max_workgroups_full_prefill(gpu):
+    d = W.make("prefill")
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], tag="maxwg-prefill-full",
+             max_workgroups=256)
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_hook_issue_complete(gpu, name):
+    """Dispatch issued on a side stream, completed on the main stream by a hook,
+    with unrelated main-stream work in between; combine then runs on the main
+    stream."""
+    d = W.make(name, T=min(W.WORKLOADS[name]["T"], 1024))
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], reuse=(name != "decode"),
+             tag="hook-%s" % name, side_stream=True)
 
 
 # ---------------------------------------------------------------- fused low-latency dispatch

@@ -60,7 +60,7 @@ def grad_w_bound(go_bits, y_rows_bits, pos):
     return gamma * b + H * 2.0 ** -126
 
 
-def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", repeat=1):
+def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", repeat=1, max_workgroups=0):
     T = idx.shape[0]
     H = c["H"]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
@@ -70,6 +70,8 @@ def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", rep
     ctx = gpu.Context(gpu.make_config(M, H, c["E"], c["R"], c["k"], 0, c["quant"], c["layout"]))
     if tune is not None:
         ctx.tune(0, tune)
+    if max_workgroups:
+        ctx.set_max_workgroups(max_workgroups)
     ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"], max_tokens=M if ll else 0,
                           with_send=not ll)
     n_pairs = ref["n_pairs"]
@@ -204,6 +206,17 @@ def test_backward_row_split(gpu, chunks):
     c["max_tokens"] = 200
     run_backward(gpu, c, d["x"], d["topk_idx"], d["topk_weights"], max_tokens=200, tune=chunks,
                  tag="chunks%d" % chunks, repeat=2)
+
+
+@pytest.mark.parametrize("max_wg", [1, 7, 100])
+def test_backward_max_workgroups(gpu, max_wg):
+    """Capped grids: each combine-backward block loops over several tokens,
+    reusing its LDS reduction buffer."""
+    c = small_cfg("prefill", H=7168)
+    d = W.make("prefill", T=300)
+    c["max_tokens"] = 300
+    run_backward(gpu, c, d["x"], d["topk_idx"], d["topk_weights"], max_tokens=300,
+                 tag="maxwg%d" % max_wg, max_workgroups=max_wg)
 
 
 @pytest.mark.parametrize("T,k,H", [(300, 1, 1024), (64, 32, 1024), (65, 17, 1024), (64, 32, 7168),
