@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="skip the 128-token decode side measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward side measurement")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="skip the GEMM-overlap side measurement (workgroup cap + hooks)")
     p.add_argument("--step", default="forward", choices=["forward", "backward"],
                    help="which step the main line times: forward (layout + dispatch + combine) or "
                         "backward (dispatch backward + combine backward)")
@@ -201,6 +203,88 @@ def timed_kernels(moe, torch, s, steps, flush=None, fn=step):
     return kt
 
 
+def overlap(moe, torch, s, fn, caps, iters=40):
+    """A bf16 GEMM [T, H] x [H, H] on the main stream while the step runs on a
+    side stream (issued there, completed on the main stream by a hook), for
+    each workgroup cap.  Reports the GEMM alone, the step alone, and per cap
+    the step alone, the overlapped iteration and the GEMM's own duration
+    inside it (events on the main stream)."""
+    c, dev = s["c"], s["x"].device
+    T, H = c["T"], c["H"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    a = torch.randn((T, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((H, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16).contiguous()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    hook = moe.Hook()
+
+    def gemm():
+        torch.matmul(a, b, out=out)
+
+    def wall(f, n):
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            f()
+        torch.cuda.synchronize()
+        return 1e6 * (time.perf_counter() - t0) / n
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+
+    def median_us():
+        return 1e3 * sorted(e0.elapsed_time(e1) for e0, e1 in ev)[iters // 2]
+
+    for _ in range(5):
+        gemm()
+    for i in range(iters):   # the GEMM alone, timed the same way as inside the overlap
+        ev[i][0].record(main)
+        gemm()
+        ev[i][1].record(main)
+    torch.cuda.synchronize()
+    gemm_us = median_us()
+    res = {"gemm": "bf16 [%d, %d] x [%d, %d]" % (T, H, H, H),
+           "gemm_tflops": round(2.0 * T * H * H / (gemm_us * 1e-6) / 1e12, 1),
+           "us_gemm_alone": round(gemm_us, 1), "caps": []}
+    for cap in caps:
+        s["ctx"].set_max_workgroups(cap)
+        step_us = wall(lambda: fn(moe, s), iters)
+
+        def both(i=None):
+            if i is not None:
+                ev[i][0].record(main)
+            gemm()
+            if i is not None:
+                ev[i][1].record(main)
+            with torch.cuda.stream(side):
+                fn(moe, s)
+            hook.record(side)
+            hook.wait(main)
+
+        for _ in range(5):
+            both()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(iters):
+            both(i)
+        torch.cuda.synchronize()
+        both_us = 1e6 * (time.perf_counter() - t0) / iters
+        g_us = median_us()
+        res["caps"].append({"max_workgroups": cap, "us_step_alone": round(step_us, 1),
+                            "us_overlapped_iteration": round(both_us, 1),
+                            "us_gemm_in_overlap": round(g_us, 1),
+                            "gemm_slowdown": round(g_us / gemm_us, 3),
+                            "serial_us": round(gemm_us + step_us, 1)})
+    s["ctx"].set_max_workgroups(0)
+    st, _ = moe.moe_poll_error(s["ctx"])
+    assert st == moe.MOE_OK, st
+    hook.close()
+    return res
+
+
 def cpu_baseline(s, reps):
     """The oracle as it stands (single-threaded scalar C) on the same inputs."""
     import numpy as np
@@ -304,6 +388,10 @@ def main():
             "kernels": kernel_table(kt_b, alg_b)}
         for key in ("grad_recv", "grad_out", "grad_x", "grad_y", "grad_w"):
             del s[key]
+        torch.cuda.empty_cache()
+
+    if not a.profile_only and not a.no_overlap and a.step == "forward":
+        line["overlap"] = overlap(moe, torch, s, fn, [0, 1024, 512, 256, 128, 64])
         torch.cuda.empty_cache()
 
     if not a.profile_only and not a.no_decode and a.workload != "decode":

@@ -16,8 +16,11 @@
 //    128-channel block), then stored with 16-byte (8-byte for fp8) stores to
 //    every destination row: up to min(k, R) send rows and k receive rows.
 //    Destination row indices are wave-uniform (readlane -> SGPR), so the store
-//    loop has no divergence.  Plain (cached) loads and stores: on MI355X they
-//    measured ~25% faster than non-temporal ones for this write-heavy kernel.
+//    loop has no divergence.  Rows are written with non-temporal stores: on
+//    MI355X they cost ~2% of the kernel's time alone, but cached stores push
+//    ~0.9 GB per prefill launch through the 256 MB Infinity Cache and slow a
+//    concurrent bf16 GEMM by 1.3x (its operands are evicted); streamed, the
+//    GEMM keeps its speed.
 //  * Combine: one wavefront per (token, row slice); for each 16-byte chunk the
 //    k routed rows are loaded together, accumulated in fp32 in slot order with
 //    separately rounded multiply and add, rounded once to bf16 (RNE).  The
@@ -321,8 +324,8 @@ __device__ __forceinline__ void store_row(V* dst, const V* v, int64_t gbase, int
     for (int i = 0; i < C; ++i) {
         const int64_t gi = gbase + i * 64;
         const ChunkState cs = chunk_state(gi, nchunk);
-        if (cs == kChunkFull) dst[gi + lane] = v[i];
-        else if (cs == kChunkPart && gi + lane < nchunk) dst[gi + lane] = v[i];
+        if (cs == kChunkFull) __builtin_nontemporal_store(v[i], dst + gi + lane);
+        else if (cs == kChunkPart && gi + lane < nchunk) __builtin_nontemporal_store(v[i], dst + gi + lane);
     }
 }
 
