@@ -370,7 +370,7 @@ def main():
         "kernels": per_kernel,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(dom, a.workload)},
+                     "traffic": traffic_for(dom, a.workload + ("_backward" if a.step == "backward" else ""))},
     }
 
     if not a.profile_only and not a.no_backward and a.step == "forward":
@@ -385,7 +385,8 @@ def main():
             "us_per_step": round(us_b, 2),
             "alg_bytes_per_step": sum(alg_b.values()),
             "GB/s": round(sum(alg_b.values()) / (us_b * 1e-6) / 1e9, 1),
-            "kernels": kernel_table(kt_b, alg_b)}
+            "kernels": kernel_table(kt_b, alg_b),
+            "traffic_bytes_per_launch": {k_: traffic_for(k_, a.workload + "_backward") for k_ in alg_b}}
         for key in ("grad_recv", "grad_out", "grad_x", "grad_y", "grad_w"):
             del s[key]
         torch.cuda.empty_cache()
