@@ -185,6 +185,34 @@ def timed(moe, torch, s, steps, warmup, fn=step):
     return wall
 
 
+def timed_graph(moe, torch, s, fn, steps_per_graph=100, replays=10):
+    """Per-step time of `steps_per_graph` steps captured in one HIP graph and
+    replayed: the GPU-side time of a step without host launch overhead (the
+    library's calls only launch kernels on the capturing stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn(moe, s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps_per_graph):
+            fn(moe, s)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st, _ = moe.moe_poll_error(s["ctx"])
+    assert st == moe.MOE_OK, st
+    del g
+    return wall / (replays * steps_per_graph)
+
+
 def timed_kernels(moe, torch, s, steps, flush=None, fn=step):
     """Per-kernel durations from the HIP events the library records around
     each of its launches, on its launch stream, over `steps` more steps.  The
@@ -403,11 +431,13 @@ def main():
         alg_d = algorithmic_bytes(sd["c"], 128, 0, sd["n_pairs"], 128 * 8)
         ll_bytes = alg_d["dispatch"] + alg_d["combine"]      # routing is read inside dispatch
         warm_us = 1e6 * wall_d / 500
+        graph_us = 1e6 * timed_graph(moe, torch, sd, step_ll)
         cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("dispatch", "combine")}
         line["decode"] = {
             "workload": "decode: T=128 H=7168 E=256 R=32 top-8 fp8 padded-LL",
             "step": "dispatch from topk_idx (one fused launch) + combine",
             "us_per_step_warm": round(warm_us, 2),
+            "us_per_step_graph": round(graph_us, 2),
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
             "alg_bytes_per_step": ll_bytes,
             "GB/s_warm": round(ll_bytes / (warm_us * 1e-6) / 1e9, 1)}

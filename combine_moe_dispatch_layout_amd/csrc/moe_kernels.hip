@@ -109,13 +109,14 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
     return v;
 }
 
-// Exclusive prefix sum of v[0..n) (n <= 4 * kBlockThreads) into out[0..n),
-// returns the total; all threads of the block must call it.  `wsum` is
-// kWavesPerBlock ints of LDS scratch.
+// Exclusive prefix sum of v[0..n) into out[0..n) for a block of NT threads,
+// returns the total; all threads of the block must call it.  `wsum` is NT / 64
+// ints of LDS scratch.
+template <int NT = kBlockThreads>
 __device__ __forceinline__ int block_exclusive_scan(const int32_t* v, int32_t* out, int n, int32_t* wsum) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int per = (n + kBlockThreads - 1) / kBlockThreads;
+    const int per = (n + NT - 1) / NT;
     const int lo = tid * per < n ? tid * per : n;
     const int hi = lo + per < n ? lo + per : n;
     int own = 0;
@@ -125,7 +126,7 @@ __device__ __forceinline__ int block_exclusive_scan(const int32_t* v, int32_t* o
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
-    for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+    for (int ww = 0; ww < NT / 64; ++ww) {
         const int s = wsum[ww];
         base += ww < w ? s : 0;
         total += s;
@@ -509,8 +510,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
 // ============================================================== fused low-latency dispatch
 // In the padded low-latency layout a slot's row is e * cap + s0 * M + (its
 // rank among the rows of expert e), so no global scan stands between the
-// routing and the copy: one launch does both.  One block per token; its 4
-// wavefronts split the row into at most 4 slices.  The block builds two LDS
+// routing and the copy: one launch does both.  One block per token (256
+// threads, or 1024 for rows of more than 256 16-byte chunks, so that a
+// 7168-wide row is one chunk per lane); its wavefronts split the row into
+// slices.  The block builds two LDS
 // histograms of the T * k routing entries -- all of them, and those of
 // earlier tokens -- with atomic adds (integer counts: order-free): a slot's
 // rank is the earlier-token count of its expert plus the earlier slots of its
@@ -518,14 +521,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
 // expert-major position (for the handle).  Block 0 also publishes the
 // handle's counts and offsets.  For T * k <= kFusedMaxEntries and
 // T <= kFusedMaxTokens.
-template <int C, bool FP8>
-__global__ __launch_bounds__(kBlockThreads) void k_ll_dispatch(PackArgs a) {
+template <int C, bool FP8, int NT>
+__global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
     __shared__ int32_t tot[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // histogram of all entries (+ ranks, block 0)
     __shared__ int32_t hb[MOE_MAX_EXPERTS];                    // histogram of entries of earlier tokens
     __shared__ int32_t off[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // exclusive scans of tot
     __shared__ unsigned long long tok_mask[kFusedMaxTokens];    // ranks of each token (block 0)
-    __shared__ int32_t wsum[kWavesPerBlock];
-    constexpr int kPerThread = kFusedMaxEntries / kBlockThreads;
+    __shared__ int32_t wsum[NT / 64];
+    constexpr int kPerThread = kFusedMaxEntries / NT;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -562,18 +565,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_ll_dispatch(PackArgs a) {
     int64_t ent[kPerThread];
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
-        const int i = u * kBlockThreads + tid;
+        const int i = u * NT + tid;
         ent[u] = i < nent ? a.topk_idx[i] : -1;
     }
-    for (int i = tid; i < E + R; i += kBlockThreads) tot[i] = 0;
-    for (int i = tid; i < E; i += kBlockThreads) hb[i] = 0;
-    if (b0) for (int i = tid; i < T; i += kBlockThreads) tok_mask[i] = 0ull;
+    for (int i = tid; i < E + R; i += NT) tot[i] = 0;
+    for (int i = tid; i < E; i += NT) hb[i] = 0;
+    if (b0) for (int i = tid; i < T; i += NT) tok_mask[i] = 0ull;
     __syncthreads();
 
     // ---- histograms (integer counts: order-free)
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
-        const int i = u * kBlockThreads + tid;
+        const int i = u * NT + tid;
         const int64_t ee = ent[u];
         if (ee >= 0 && ee < E) {
             atomicAdd(&tot[(int)ee], 1);
@@ -585,18 +588,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_ll_dispatch(PackArgs a) {
     }
     __syncthreads();
     if (b0) {   // tokens per rank
-        for (int i = tid; i < T; i += kBlockThreads)
+        for (int i = tid; i < T; i += NT)
             for (uint64_t m = tok_mask[i]; m != 0; m &= m - 1) atomicAdd(&tot[E + __ffsll((unsigned long long)m) - 1], 1);
         __syncthreads();
     }
-    const int total_e = block_exclusive_scan(tot, off, E, wsum);   // off[e] = entries with a smaller id
+    const int total_e = block_exclusive_scan<NT>(tot, off, E, wsum);   // off[e] = entries with a smaller id
     if (b0) {
-        const int total_r = block_exclusive_scan(tot + E, off + E, R, wsum);
-        for (int ee = tid; ee < E; ee += kBlockThreads) {
+        const int total_r = block_exclusive_scan<NT>(tot + E, off + E, R, wsum);
+        for (int ee = tid; ee < E; ee += NT) {
             a.h_eoff[ee] = off[ee];
             a.h_recv_counts[ee] = tot[ee];
         }
-        for (int r = tid; r < R; r += kBlockThreads) a.h_roff[r] = off[E + r];
+        for (int r = tid; r < R; r += NT) a.h_roff[r] = off[E + r];
         if (tid == 0) {
             a.h_eoff[E] = total_e;
             a.h_roff[R] = total_r;
@@ -907,22 +910,24 @@ hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool se
     }
 }
 
-hipError_t launch_ll_fused(const PackArgs& a, int chunks, bool fp8, hipStream_t s) {
+hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8, hipStream_t s) {
     const dim3 grid(a.T > 0 ? (unsigned)a.T : 1u);   // one block per token
-#define MOE_LL_CASE(CC)                                                                              \
-    case CC:                                                                                          \
-        if (fp8) hipLaunchKernelGGL((k_ll_dispatch<CC, true>), grid, dim3(kBlockThreads), 0, s, a);  \
-        else hipLaunchKernelGGL((k_ll_dispatch<CC, false>), grid, dim3(kBlockThreads), 0, s, a);     \
-        return hipGetLastError();
-    switch (chunks) {
-        MOE_LL_CASE(1)
-        MOE_LL_CASE(2)
-        MOE_LL_CASE(4)
-        MOE_LL_CASE(8)
-        MOE_LL_CASE(16)
-        default: return hipErrorInvalidValue;
+#define MOE_LL_CASE(CC, NT)                                                                          \
+    if (chunks == CC && threads == NT) {                                                              \
+        if (fp8) hipLaunchKernelGGL((k_ll_dispatch<CC, true, NT>), grid, dim3(NT), 0, s, a);          \
+        else hipLaunchKernelGGL((k_ll_dispatch<CC, false, NT>), grid, dim3(NT), 0, s, a);             \
+        return hipGetLastError();                                                                     \
     }
+    MOE_LL_CASE(1, 256)
+    MOE_LL_CASE(2, 256)
+    MOE_LL_CASE(4, 256)
+    MOE_LL_CASE(8, 256)
+    MOE_LL_CASE(16, 256)
+    MOE_LL_CASE(1, 1024)
+    MOE_LL_CASE(2, 1024)
+    MOE_LL_CASE(4, 1024)
 #undef MOE_LL_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {

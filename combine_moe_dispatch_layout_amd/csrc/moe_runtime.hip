@@ -470,13 +470,15 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH);
     hipError_t e;
     if (fused) {
-        // one block per token, its 4 wavefronts split the row into <= 4 slices
-        // (the context's layout state is neither read nor written here)
+        // one block per token whose wavefronts split the row into slices: 1024
+        // threads when the row has more than 256 chunks (the context's layout
+        // state is neither read nor written here)
         const int64_t nchunk = c.hidden / 8;
+        const int nt = nchunk > kBlockThreads ? 1024 : kBlockThreads;
         int cf = 1;
-        while (cf < 16 && (int64_t)kBlockThreads * cf < nchunk) cf *= 2;
+        while (cf < 16 && (int64_t)nt * cf < nchunk) cf *= 2;
         a.nslices = (int)((nchunk + 64 * cf - 1) / (64 * cf));
-        e = launch_ll_fused(a, cf, fp8, s);
+        e = launch_ll_fused(a, cf, nt, fp8, s);
     } else if (num_tokens == 0) {
         // grid of one block: block 0 copies the offsets, every wave exits (no items)
         a0.nslices = 1;

@@ -416,8 +416,11 @@ def test_hook_issue_complete(gpu, name):
 # that it falls back to layout + pack.  Both must give the same results as the oracle.
 @pytest.mark.parametrize("quant", [W.QUANT_FP8, W.QUANT_BF16])
 @pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 200, 255, 256, 257])
-def test_ll_fused_ragged(gpu, T, quant):
-    c = small_cfg("decode")
+@pytest.mark.parametrize("H", [512, 7168])
+def test_ll_fused_ragged(gpu, T, quant, H):
+    """512-wide rows run 256-thread blocks, 7168-wide rows 1024-thread blocks
+    (one 16-byte chunk per lane)."""
+    c = small_cfg("decode", H=H)
     c["quant"] = quant
     d = W.make("decode", T=T)
     M = max(T, 1)
@@ -426,15 +429,16 @@ def test_ll_fused_ragged(gpu, T, quant):
              max_tokens=M, tag="ll-fused-%d" % quant)
 
 
-@pytest.mark.parametrize("T,k", [(512, 4), (513, 2), (2048, 1), (64, 32), (65, 32), (1000, 2)])
-def test_ll_fused_topk_extremes(gpu, T, k):
-    c = dict(index=11, T=T, H=256, E=64, R=8, k=k, quant=W.QUANT_FP8,
+@pytest.mark.parametrize("T,k,H", [(512, 4, 256), (513, 2, 256), (2048, 1, 256), (64, 32, 256), (65, 32, 256),
+                                   (1000, 2, 256), (256, 8, 4096), (64, 32, 2176), (100, 3, 32768)])
+def test_ll_fused_topk_extremes(gpu, T, k, H):
+    c = dict(index=11, T=T, H=H, E=64, R=8, k=k, quant=W.QUANT_FP8,
              layout=W.LAYOUT_PADDED_LL, max_tokens=T)
     rng = np.random.Generator(np.random.PCG64(T + k))
     idx = W.route_uniform(rng, T, c["E"], k)
     x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
-    run_case(gpu, c, x, idx, w, reuse=False, max_tokens=T, tag="ll-fused-k%d" % k)
+    run_case(gpu, c, x, idx, w, reuse=False, max_tokens=T, tag="ll-fused-k%d-H%d" % (k, H))
 
 
 def test_ll_fused_irregular_routing(gpu):
