@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="skip the 128-token decode side measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward side measurement")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-config table (all five workloads, warm step time)")
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the GEMM-overlap side measurement (workgroup cap + hooks)")
     p.add_argument("--step", default="forward", choices=["forward", "backward"],
@@ -313,11 +315,71 @@ def overlap(moe, torch, s, fn, caps, iters=40):
     return res
 
 
+def copy_reference(torch, nbytes=1 << 30, reps=20):
+    """Achievable HBM rate of a plain 1 GiB device-to-device copy on this machine
+    (read + write bytes / time, HIP events on the current stream)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (us * 1e-6) / 1e9
+
+
+def all_configs(moe, W, torch, steps=50):
+    """Warm step time and algorithmic GB/s of every workload (the layout-reusing
+    step for the contiguous layout, the fused low-latency step for the padded one)."""
+    out = {}
+    for name in ("tiny", "decode", "prefill", "grouped", "skewed"):
+        s = setup(moe, W, torch, name)
+        c = s["c"]
+        T = c["T"]
+        alg = algorithmic_bytes(c, T, s["n_send"], s["n_pairs"], T * c["k"])
+        fn = step
+        if c["layout"] == 1:
+            fn = step_ll
+            alg["layout"] = 0
+        us = 1e6 * timed(moe, torch, s, steps, 10, fn=fn) / steps
+        b = sum(alg.values())
+        out[name] = {"T": T, "H": c["H"], "E": c["E"], "R": c["R"], "k": c["k"],
+                     "mode": ("fp8 " if c["quant"] else "bf16 ") + ("padded-LL" if c["layout"] else "send+contiguous"),
+                     "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                     "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        s["ctx"].close()
+        del s
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(s, reps):
     """The oracle as it stands (single-threaded scalar C) on the same inputs."""
     import numpy as np
     import oracle
     d, c = s["d"], s["c"]
+    # one host core, like the single-threaded oracle it times
+    saved = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(saved)})
     y = s["y"][:s["n_pairs"]].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
     times = []
     for _ in range(reps):
@@ -325,6 +387,7 @@ def cpu_baseline(s, reps):
         r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
         oracle.combine(y, d["topk_weights"], r["pos"])
         times.append(time.perf_counter() - t0)
+    os.sched_setaffinity(0, saved)
     return float(np.median(times)), r
 
 
@@ -445,13 +508,24 @@ def main():
         del sd, flush
         torch.cuda.empty_cache()
 
+    if not a.profile_only:
+        cp = copy_reference(torch)
+        line["copy_reference"] = {"GB/s": round(cp, 1), "what": "1 GiB device-to-device copy, read + write bytes",
+                                  "step_frac_of_copy": round(value / cp, 3),
+                                  "dominant_kernel_frac_of_copy": round(achieved / cp, 3)}
+
+    if not a.profile_only and not a.no_configs and a.step == "forward":
+        line["configs"] = all_configs(moe, W, torch)
+
     if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
+        model, ncpu = host_cpu()
         sec, _ = cpu_baseline(s, a.cpu_reps)
         line["cpu_baseline"] = {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle",
                                 "sample": "the full %s workload (%d tokens): layout, positions, payload "
                                           "rows and combine in the scalar C oracle, median of %d runs, "
-                                          "%.2f s each" % (a.workload, T, a.cpu_reps, sec)}
+                                          "%.2f s each, pinned to one of %d host cores (%s)" % (
+                                              a.workload, T, a.cpu_reps, sec, ncpu, model)}
     print(json.dumps(line), flush=True)
     s["ctx"].close()
 

@@ -144,6 +144,8 @@ struct moe_ctx {
     int pack_chunks, combine_chunks;
     // cap on the workgroups of the high-throughput kernels (0 = none)
     int max_blocks;
+    // host-side launch log on stderr (environment MOE_EP_LOG=1 at context creation)
+    bool log;
     // timing
     bool timing;
     int max_launches;
@@ -163,12 +165,21 @@ bool on_ctx_device(const moe_ctx* ctx) {
     return hipGetDevice(&dev) == hipSuccess && dev == ctx->device;
 }
 
-// Record timing events around one launch when timing is on.
+const char* kernel_name(int id) {
+    static const char* names[MOE_KERNEL_COUNT] = {"layout", "dispatch", "combine", "dispatch_backward",
+                                                  "combine_backward"};
+    return id >= 0 && id < MOE_KERNEL_COUNT ? names[id] : "?";
+}
+
+// Record timing events around one launch when timing is on; log it when asked.
 struct TimedLaunch {
     moe_ctx* ctx;
     hipStream_t s;
     int slot;
     TimedLaunch(moe_ctx* c, hipStream_t st, int id) : ctx(c), s(st), slot(-1) {
+        if (c->log)
+            std::fprintf(stderr, "[moe_ep] ctx %p: %s on stream %p (max_workgroups %d)\n", static_cast<void*>(c),
+                         kernel_name(id), static_cast<void*>(st), c->max_blocks);
         if (c->timing && (int)c->kid.size() < c->max_launches) {
             slot = (int)c->kid.size();
             c->kid.push_back(id);
@@ -292,6 +303,10 @@ MOE_API moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out) {
     ctx->pack_chunks = 0;
     ctx->combine_chunks = 0;
     ctx->max_blocks = 0;
+    {
+        const char* v = std::getenv("MOE_EP_LOG");
+        ctx->log = v != nullptr && v[0] == '1';
+    }
     ctx->timing = false;
     ctx->max_launches = 0;
     if (hipMalloc(reinterpret_cast<void**>(&ctx->ws), ctx->wl.total) != hipSuccess) {

@@ -39,6 +39,9 @@
  *    the offending slot is then treated as empty (-1).
  *  - bf16 buffers are passed as raw 16-bit storage; fp8 buffers hold OCP
  *    E4M3FN codes, one byte per channel.
+ *  - With MOE_EP_LOG=1 in the environment when a context is created, each
+ *    kernel launch of that context is logged on stderr (host side only; no
+ *    effect on results).
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H

@@ -516,3 +516,14 @@ def test_graph_capture_replays_match_eager(gpu, name, reuse):
     assert st == gpu.MOE_OK
     del g
     ctx.close()
+
+
+def test_launch_log(gpu, capfd, monkeypatch):
+    """MOE_EP_LOG=1 at context creation logs each launch on stderr; results unchanged."""
+    monkeypatch.setenv("MOE_EP_LOG", "1")
+    d = W.make("tiny")
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], tag="log")
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    for name in ("layout on", "dispatch on", "combine on"):
+        assert "[moe_ep]" in err and name in err, err[-2000:]
