@@ -157,13 +157,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int E = a.E, R = a.R, k = a.k;
     const int ntiles = gridDim.x;
-    for (int i = tid; i < kWavesPerBlock * E; i += kBlockThreads) {
-        peer_mask[i] = 0ull;
-        hist_e[i] = 0;
-    }
-    for (int i = tid; i < kWavesPerBlock * R; i += kBlockThreads) rank_toks[i] = 0ull;
-    tok_mask[tid] = 0ull;
-
     const int64_t tok0 = (int64_t)blockIdx.x * kTileTokens + w * 64;   // this wave's first token
     const int64_t t = tok0 + lane;
     const bool tok_ok = t < a.T;
@@ -172,19 +165,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     const int64_t ent0 = tok0 * k;
     const uint64_t below = lanes_below(lane);
 
-    // ---- all loads of this wave's entries first (independent, in flight together)
-    int ev[KMAX];
+    // ---- all loads of this wave's entries first, in flight together (nothing
+    // with a side effect between them), then the LDS is cleared meanwhile
+    int64_t raw[KMAX];
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) {
         const int64_t i = (int64_t)c * 64 + lane;
-        int e = -1;
-        if (c < k && i < nent) {
-            const int64_t v = a.topk_idx[ent0 + i];
-            if (v >= 0 && v < E) e = (int)v;
-            else if (v != -1) atomicOr(a.err, kErrBadTopk);
-        }
-        ev[c] = e;
+        raw[c] = c < k && i < nent ? a.topk_idx[ent0 + i] : -1;
     }
+    for (int i = tid; i < kWavesPerBlock * E; i += kBlockThreads) {
+        peer_mask[i] = 0ull;
+        hist_e[i] = 0;
+    }
+    for (int i = tid; i < kWavesPerBlock * R; i += kBlockThreads) rank_toks[i] = 0ull;
+    tok_mask[tid] = 0ull;
+    int ev[KMAX];
+    bool bad = false;
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) {
+        const int64_t v = raw[c];
+        const bool ok = v >= 0 && v < E;
+        bad |= !ok && v != -1;
+        ev[c] = ok ? (int)v : -1;
+    }
+    if (bad) atomicOr(a.err, kErrBadTopk);
     __syncthreads();
 
     // ---- phase 1: for every 64-entry chunk (row-major order), the lanes holding
@@ -227,6 +231,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     // grand totals for the last block)
     for (int i = tid; i < kWavesPerBlock * R; i += kBlockThreads) hist_r[i] = __popcll(rank_toks[i]);
     __syncthreads();
+    int seen = 0;   // returned totals: using them makes the adds complete before the arrival below
     for (int col = tid; col < E + R; col += kBlockThreads) {
         const bool is_e = col < E;
         int32_t* h = is_e ? hist_e + col : hist_r + (col - E);
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
             tot[col] = run;
         } else {
             a.tile_cnt[(int64_t)col * a.tile_stride + blockIdx.x] = run;
-            if (run != 0) atomicAdd(&a.grand_tot[col], run);
+            if (run != 0) seen |= atomicAdd(&a.grand_tot[col], run);
         }
     }
     __syncthreads();
@@ -273,14 +278,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
         }
     }
 
-    // ---- arrival: the last block reads (and resets) the grand totals
+    // ---- arrival: the last block reads (and resets) the grand totals.  Only
+    // device-scope atomics cross blocks here (the totals, read back with atomic
+    // loads, and the arrival counter); each block's adds have completed before
+    // it arrives, so no memory fence is needed -- on this chip a device-scope
+    // release fence writes back the whole L2.
     if (ntiles > 1) {
-        __threadfence();
+        if (seen == -1) s_last = 2;   // never true: consumes the returned totals
         __syncthreads();
         if (tid == 0) s_last = (atomicAdd(a.done, 1u) == (unsigned)ntiles - 1);
         __syncthreads();
         if (!s_last) return;
-        __threadfence();
         for (int col = tid; col < E + R; col += kBlockThreads) {
             tot[col] = __hip_atomic_load(&a.grand_tot[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             a.grand_tot[col] = 0;
