@@ -112,7 +112,8 @@ hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool se
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s);
 // Low-latency dispatch without a separate layout launch (T * k <= kFusedMaxEntries,
-// T <= kFusedMaxTokens); one block of `threads` (256 or 1024) per token.
+// T <= kFusedMaxTokens); a summary block plus one block of `threads` (256 or
+// 1024) per token.
 hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8, hipStream_t s);
 
 }  // namespace moe

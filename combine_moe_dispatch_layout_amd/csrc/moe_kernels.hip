@@ -518,39 +518,89 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
 // ============================================================== fused low-latency dispatch
 // In the padded low-latency layout a slot's row is e * cap + s0 * M + (its
 // rank among the rows of expert e), so no global scan stands between the
-// routing and the copy: one launch does both.  One block per token (256
-// threads, or 1024 for rows of more than 256 16-byte chunks, so that a
-// 7168-wide row is one chunk per lane); its wavefronts split the row into
-// slices.  The block builds two LDS
-// histograms of the T * k routing entries -- all of them, and those of
-// earlier tokens -- with atomic adds (integer counts: order-free): a slot's
-// rank is the earlier-token count of its expert plus the earlier slots of its
-// own token, and the exclusive scan of the full histogram gives its
-// expert-major position (for the handle).  Block 0 also publishes the
-// handle's counts and offsets.  For T * k <= kFusedMaxEntries and
-// T <= kFusedMaxTokens.
+// routing and the copy: one launch does both.  Grid = T + 1 blocks.
+//  * Blocks 1..T: one token each (256 threads, or 1024 for rows of more than
+//    256 16-byte chunks, so that a 7168-wide row is one chunk per lane); the
+//    wavefronts split the row into slices.  A slot of expert e needs two
+//    counts over the T * k routing entries: entries of e in earlier tokens
+//    (its rank, plus earlier slots of its own token with the same expert) and
+//    valid entries with a smaller expert id (its expert-major position, for
+//    the handle's recv_src_idx).  Each wavefront counts its share of the
+//    entries against the token's k experts with ballots; one barrier and a
+//    sum over the wavefronts give both counts (integer sums: order-free).
+//  * Block 0: the handle's summary -- per-expert counts (an LDS histogram of
+//    all entries), their exclusive scan, tokens per rank and its scan -- and
+//    the bad-id flag.
+// For T * k <= kFusedMaxEntries and T <= kFusedMaxTokens.
+template <int NT>
+__device__ __forceinline__ void ll_summary(const PackArgs& a) {
+    __shared__ int32_t tot[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // entries per expert, then tokens per rank
+    __shared__ int32_t off[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // exclusive scans of tot
+    __shared__ unsigned long long tok_mask[kFusedMaxTokens];    // ranks of each token
+    __shared__ int32_t wsum[NT / 64];
+    constexpr int kPerThread = kFusedMaxEntries / NT;
+    const int tid = threadIdx.x;
+    const int k = a.k, E = a.E, R = a.R, T = a.T;
+    const int nent = T * k;
+    int64_t ent[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = u * NT + tid;
+        ent[u] = i < nent ? a.topk_idx[i] : -1;
+    }
+    for (int i = tid; i < E + R; i += NT) tot[i] = 0;
+    for (int i = tid; i < T; i += NT) tok_mask[i] = 0ull;
+    __syncthreads();
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = u * NT + tid;
+        const int64_t ee = ent[u];
+        if (ee >= 0 && ee < E) {
+            atomicAdd(&tot[(int)ee], 1);
+            atomicOr(&tok_mask[i / k], 1ull << ((int)ee / a.El));
+        } else if (i < nent && ee != -1) {
+            bad = true;
+        }
+    }
+    if (bad) atomicOr(a.err, kErrBadTopk);
+    __syncthreads();
+    for (int i = tid; i < T; i += NT)
+        for (uint64_t m = tok_mask[i]; m != 0; m &= m - 1) atomicAdd(&tot[E + __ffsll((unsigned long long)m) - 1], 1);
+    __syncthreads();
+    const int total_e = block_exclusive_scan<NT>(tot, off, E, wsum);
+    const int total_r = block_exclusive_scan<NT>(tot + E, off + E, R, wsum);
+    for (int ee = tid; ee < E; ee += NT) {
+        a.h_eoff[ee] = off[ee];
+        a.h_recv_counts[ee] = tot[ee];
+    }
+    for (int r = tid; r < R; r += NT) a.h_roff[r] = off[E + r];
+    if (tid == 0) {
+        a.h_eoff[E] = total_e;
+        a.h_roff[R] = total_r;
+    }
+}
+
 template <int C, bool FP8, int NT>
 __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
-    __shared__ int32_t tot[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // histogram of all entries (+ ranks, block 0)
-    __shared__ int32_t hb[MOE_MAX_EXPERTS];                    // histogram of entries of earlier tokens
-    __shared__ int32_t off[MOE_MAX_EXPERTS + MOE_MAX_RANKS];   // exclusive scans of tot
-    __shared__ unsigned long long tok_mask[kFusedMaxTokens];    // ranks of each token (block 0)
-    __shared__ int32_t wsum[NT / 64];
+    if (blockIdx.x == 0) {
+        ll_summary<NT>(a);
+        return;
+    }
+    __shared__ int32_t cnt_hb[NT / 64][MOE_MAX_TOPK];    // per wavefront: entries of e_j in earlier tokens
+    __shared__ int32_t cnt_lt[NT / 64][MOE_MAX_TOPK];    // per wavefront: valid entries with id < e_j
     constexpr int kPerThread = kFusedMaxEntries / NT;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int k = a.k, E = a.E, R = a.R, T = a.T;
-    const int nent = T * k;
-    const uint64_t below = lanes_below(lane);
-    const int t = blockIdx.x;                 // this block's token
-    const bool has_token = t < T;
+    const int k = a.k, E = a.E;
+    const int nent = a.T * k;
+    const int t = blockIdx.x - 1;             // this block's token
     const int s = w;                          // this wavefront's row slice
-    const bool has_slice = has_token && s < a.nslices;
+    const bool has_slice = s < a.nslices;
     const int before = t * k;                 // entries of earlier tokens
-    const bool b0 = blockIdx.x == 0;
 
-    // ---- row slice and routing entries, all loads issued first
+    // ---- row slice, the token's own slots and the routing entries: all loads first
     const int64_t nchunk = a.H / 8;
     const int64_t gbase = (int64_t)s * 64 * C;
     const int64_t g0 = gbase + lane;
@@ -565,68 +615,47 @@ __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
             if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) v[i] = src[g];
         }
     }
-    int e = -1;
-    if (has_token && lane < k) {
-        const int64_t vv = a.topk_idx[(int64_t)before + lane];
-        if (vv >= 0 && vv < E) e = (int)vv;
-    }
+    int64_t mine = -1;
+    if (lane < k) mine = a.topk_idx[(int64_t)before + lane];
     int64_t ent[kPerThread];
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
         const int i = u * NT + tid;
         ent[u] = i < nent ? a.topk_idx[i] : -1;
     }
-    for (int i = tid; i < E + R; i += NT) tot[i] = 0;
-    for (int i = tid; i < E; i += NT) hb[i] = 0;
-    if (b0) for (int i = tid; i < T; i += NT) tok_mask[i] = 0ull;
-    __syncthreads();
+    const int e = mine >= 0 && mine < E ? (int)mine : -1;   // lane j < k: expert of slot j
 
-    // ---- histograms (integer counts: order-free)
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        const int i = u * NT + tid;
-        const int64_t ee = ent[u];
-        if (ee >= 0 && ee < E) {
-            atomicAdd(&tot[(int)ee], 1);
-            if (i < before) atomicAdd(&hb[(int)ee], 1);
-            if (b0) atomicOr(&tok_mask[i / k], 1ull << ((int)ee / a.El));
-        } else if (b0 && i < nent && ee != -1) {
-            atomicOr(a.err, kErrBadTopk);
-        }
-    }
-    __syncthreads();
-    if (b0) {   // tokens per rank
-        for (int i = tid; i < T; i += NT)
-            for (uint64_t m = tok_mask[i]; m != 0; m &= m - 1) atomicAdd(&tot[E + __ffsll((unsigned long long)m) - 1], 1);
-        __syncthreads();
-    }
-    const int total_e = block_exclusive_scan<NT>(tot, off, E, wsum);   // off[e] = entries with a smaller id
-    if (b0) {
-        const int total_r = block_exclusive_scan<NT>(tot + E, off + E, R, wsum);
-        for (int ee = tid; ee < E; ee += NT) {
-            a.h_eoff[ee] = off[ee];
-            a.h_recv_counts[ee] = tot[ee];
-        }
-        for (int r = tid; r < R; r += NT) a.h_roff[r] = off[E + r];
-        if (tid == 0) {
-            a.h_eoff[E] = total_e;
-            a.h_roff[R] = total_r;
-        }
-    }
-    if (!has_slice) return;
-
-    // ---- rank among the rows of its expert: earlier tokens + earlier slots of this token
-    int rank = 0, lessv = 0;
+    // ---- this wavefront's share of the two counts, for every slot of the token
     for (int j = 0; j < k; ++j) {
         const int ej = readlane(e, j);
-        if (ej >= 0) {
-            const uint64_t m = __ballot(lane < k && e == ej);
-            if (lane == j) rank = __popcll(m & below);
+        if (ej < 0) continue;
+        int c_hb = 0, c_lt = 0;
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int i = u * NT + tid;
+            c_hb += __popcll(__ballot(ent[u] == ej && i < before));
+            c_lt += __popcll(__ballot(ent[u] >= 0 && ent[u] < ej));
+        }
+        if (lane == 0) {
+            cnt_hb[w][j] = c_hb;
+            cnt_lt[w][j] = c_lt;
         }
     }
-    if (e >= 0) {
-        rank += hb[e];
-        lessv = off[e];
+    __syncthreads();
+    if (!has_slice) return;
+
+    // ---- slot j (lane j): rank among the rows of its expert and expert-major position
+    int rank = 0, lessv = 0;
+    if (lane < k && e >= 0) {
+#pragma unroll
+        for (int q = 0; q < NT / 64; ++q) {
+            rank += cnt_hb[q][lane];
+            lessv += cnt_lt[q][lane];
+        }
+    }
+    for (int j = 0; j < k; ++j) {             // earlier slots of this token with the same expert
+        const int ej = readlane(e, j);
+        rank += (j < lane && ej == e && e >= 0) ? 1 : 0;
     }
     int rrow = -1;
     if (e >= 0) {
@@ -919,7 +948,7 @@ hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool se
 }
 
 hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8, hipStream_t s) {
-    const dim3 grid(a.T > 0 ? (unsigned)a.T : 1u);   // one block per token
+    const dim3 grid((unsigned)a.T + 1u);   // block 0: the handle's summary; then one block per token
 #define MOE_LL_CASE(CC, NT)                                                                          \
     if (chunks == CC && threads == NT) {                                                              \
         if (fp8) hipLaunchKernelGGL((k_ll_dispatch<CC, true, NT>), grid, dim3(NT), 0, s, a);          \
