@@ -60,20 +60,21 @@ def grad_w_bound(go_bits, y_rows_bits, pos):
     return gamma * b + H * 2.0 ** -126
 
 
-def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", repeat=1, max_workgroups=0):
+def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", repeat=1, max_workgroups=0,
+                 src_rank=0):
     T = idx.shape[0]
     H = c["H"]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
     log("backward case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d tune=%s" %
         (tag, T, H, c["E"], c["R"], c["k"], c["quant"], c["layout"], tune))
     M = max_tokens if max_tokens is not None else max(c["max_tokens"], T, 1)
-    ctx = gpu.Context(gpu.make_config(M, H, c["E"], c["R"], c["k"], 0, c["quant"], c["layout"]))
+    ctx = gpu.Context(gpu.make_config(M, H, c["E"], c["R"], c["k"], src_rank, c["quant"], c["layout"]))
     if tune is not None:
         ctx.tune(0, tune)
     if max_workgroups:
         ctx.set_max_workgroups(max_workgroups)
     ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"], max_tokens=M if ll else 0,
-                          with_send=not ll)
+                          src_rank=src_rank, with_send=not ll)
     n_pairs = ref["n_pairs"]
     pos = ref["pos"]                                     # expert-major row of each slot
     dst_np = ref["pos_ll"] if ll else ref["pos"]         # row in the GPU receive layout
