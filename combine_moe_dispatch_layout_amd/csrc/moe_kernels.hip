@@ -5,11 +5,11 @@
 // destination, combine reads every expert-output row once and writes each
 // token row once.  Design points:
 //  * Layout: one block per 256-token tile, 4 wavefronts of 64 tokens.  Stable
-//    (token, slot) ranks come from a wavefront "match-any" (one ballot per key
-//    bit) plus per-wavefront LDS histograms -- no atomics decide any order, so
-//    results are deterministic.  The last tile block to arrive (device-scope
-//    counter) scans the per-tile histograms into global row bases, so count and
-//    scan are one launch.
+//    (token, slot) ranks come from per-expert lane masks built with LDS ORs
+//    (the lanes holding one expert find each other) plus per-wavefront LDS
+//    histograms -- no atomic decides any order, so results are deterministic.
+//    The last tile block to arrive (device-scope counter) scans the tile
+//    totals into global row bases, so count and scan are one launch.
 //  * Dispatch: one wavefront per (token, row slice).  The slice is loaded once
 //    into registers with 16-byte loads, optionally quantised to E4M3 in
 //    registers (block amax by cross-lane max over the 16 lanes holding one
@@ -27,6 +27,10 @@
 //    expert outputs are read exactly once, so they use non-temporal loads
 //    (measured ~35% faster than cached loads here); short slices (2 chunks per
 //    lane) keep many small wavefronts in flight.
+//  * Fused low-latency dispatch (decode-sized batches, padded layout): one
+//    launch computes the routing counts, the slot positions and the handle and
+//    copies the rows; no grid-wide scan is needed because a padded slot's row
+//    depends only on counts of earlier tokens.
 //  * Backward: dispatch backward is the combine kernel with unit weights (the
 //    adjoint of copying a token to k rows is adding those k rows back).  The
 //    combine backward kernel has combine's shape: it reads the output gradient

@@ -629,12 +629,23 @@ MOE_API moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags) {
 
 MOE_API moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches) {
     if (ctx == nullptr || max_launches < 1 || ctx->timing) return MOE_ERR_INVALID_ARG;
-    ctx->ev0.resize(max_launches);
-    ctx->ev1.resize(max_launches);
+    ctx->ev0.clear();
+    ctx->ev1.clear();
+    ctx->ev0.reserve(max_launches);
+    ctx->ev1.reserve(max_launches);
     for (int i = 0; i < max_launches; ++i) {
-        if (hipEventCreate(&ctx->ev0[i]) != hipSuccess || hipEventCreate(&ctx->ev1[i]) != hipSuccess) {
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+            // release what was created; the context stays without timing
+            if (a != nullptr) (void)hipEventDestroy(a);
+            for (hipEvent_t e : ctx->ev0) (void)hipEventDestroy(e);
+            for (hipEvent_t e : ctx->ev1) (void)hipEventDestroy(e);
+            ctx->ev0.clear();
+            ctx->ev1.clear();
             return MOE_ERR_HIP;
         }
+        ctx->ev0.push_back(a);
+        ctx->ev1.push_back(b);
     }
     ctx->kid.clear();
     ctx->kid.reserve(max_launches);
