@@ -495,12 +495,22 @@ def main():
         ll_bytes = alg_d["dispatch"] + alg_d["combine"]      # routing is read inside dispatch
         warm_us = 1e6 * wall_d / 500
         graph_us = 1e6 * timed_graph(moe, torch, sd, step_ll)
+        # the same step through prepared calls (arguments marshalled once): what a
+        # lean host loop sees, launch overhead included
+        pd = moe.prepare_dispatch(sd["ctx"], sd["x"], sd["idx"], False, sd["bufs"], sd["h"])
+        pc = moe.prepare_combine(sd["ctx"], sd["y"], sd["w"], sd["h"], sd["out"], sd["c"]["T"])
+
+        def step_prepared(moe_, s_):
+            pd()
+            pc()
+        prep_us = 1e6 * timed(moe, torch, sd, 500, 50, fn=step_prepared) / 500
         cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("dispatch", "combine")}
         line["decode"] = {
             "workload": "decode: T=128 H=7168 E=256 R=32 top-8 fp8 padded-LL",
             "step": "dispatch from topk_idx (one fused launch) + combine",
             "us_per_step_warm": round(warm_us, 2),
             "us_per_step_graph": round(graph_us, 2),
+            "us_per_step_prepared_calls": round(prep_us, 2),
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
             "alg_bytes_per_step": ll_bytes,
             "GB/s_warm": round(ll_bytes / (warm_us * 1e-6) / 1e9, 1)}

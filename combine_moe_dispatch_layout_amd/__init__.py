@@ -15,4 +15,5 @@ from ._binding import (  # noqa: F401
     MOE_KERNEL_COMBINE, MOE_KERNEL_COMBINE_BWD, MOE_KERNEL_DISPATCH, MOE_KERNEL_DISPATCH_BWD,
     MOE_KERNEL_LAYOUT, MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_PADDED_LL, MOE_OK, MOE_QUANT_BF16,
     MOE_QUANT_FP8_E4M3, load_library, make_config, moe_combine, moe_combine_backward, moe_dispatch,
-    moe_dispatch_backward, moe_dispatch_layout, moe_poll_error, moe_size_hint, status_str)
+    moe_dispatch_backward, moe_dispatch_layout, moe_poll_error, moe_size_hint, prepare_combine,
+    prepare_dispatch, status_str)

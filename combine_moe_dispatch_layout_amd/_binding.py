@@ -379,6 +379,54 @@ def moe_combine_backward(ctx, grad_out, topk_weights, expert_out, handle, grad_e
     return grad_expert_out, grad_weights
 
 
+# ---------------------------------------------------------------- prepared calls
+# For tight host loops (decode steps): the arguments of a call are checked and
+# marshalled once, and the returned callable only makes the C call, on the
+# stream that was current when it was prepared.  The tensors must stay alive
+# and keep their storage while the callable is used.
+def prepare_dispatch(ctx, x, topk_idx, reuse_layout, bufs, handle, stream=None):
+    c = ctx.cfg
+    _as_dev(x, torch.bfloat16, "x")
+    _as_dev(topk_idx, torch.int64, "topk_idx")
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != c.hidden or tuple(topk_idx.shape) != (T, c.topk):
+        raise ValueError("x must be [T, %d] and topk_idx [T, %d]" % (c.hidden, c.topk))
+    f = load_library().moe_dispatch
+    args = (ctx.handle, _ptr(x), _ptr(topk_idx), ctypes.c_int32(T), ctypes.c_int32(int(bool(reuse_layout))),
+            ctypes.byref(bufs.c), ctypes.byref(handle.c), _stream(stream))
+
+    def call():
+        st = f(*args)
+        if st != MOE_OK:
+            raise MoeError(st, "moe_dispatch")
+    return call
+
+
+def prepare_combine(ctx, expert_out, topk_weights, handle, out, num_tokens, stream=None):
+    """num_tokens: the token count of the dispatch whose handle is combined
+    (checked against the handle at every call)."""
+    c = ctx.cfg
+    _as_dev(expert_out, torch.bfloat16, "expert_out")
+    _as_dev(topk_weights, torch.float32, "topk_weights")
+    _as_dev(out, torch.bfloat16, "out")
+    if tuple(topk_weights.shape) != (num_tokens, c.topk) or out.numel() < num_tokens * c.hidden:
+        raise ValueError("topk_weights must be [%d, %d] and out hold [%d, %d]" % (num_tokens, c.topk, num_tokens,
+                                                                                 c.hidden))
+    if expert_out.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
+        raise ValueError("expert_out smaller than MOE_BUF_EXPERT_OUT")
+    f = load_library().moe_combine
+    hc = handle.c
+    args = (ctx.handle, _ptr(expert_out), _ptr(topk_weights), ctypes.byref(hc), _ptr(out), _stream(stream))
+
+    def call():
+        if hc.num_tokens != num_tokens:
+            raise ValueError("handle holds %d tokens, prepared for %d" % (hc.num_tokens, num_tokens))
+        st = f(*args)
+        if st != MOE_OK:
+            raise MoeError(st, "moe_combine")
+    return call
+
+
 def moe_poll_error(ctx):
     """Synchronizes the current stream; returns (status, raw flags) and clears them."""
     flags = ctypes.c_uint32(0)

@@ -527,3 +527,40 @@ def test_launch_log(gpu, capfd, monkeypatch):
     err = capfd.readouterr().err
     for name in ("layout on", "dispatch on", "combine on"):
         assert "[moe_ep]" in err and name in err, err[-2000:]
+
+
+def test_prepared_calls_match(gpu):
+    """prepare_dispatch / prepare_combine give the same bytes as the plain calls."""
+    d = W.make("decode")
+    c = d["cfg"]
+    ctx = make_ctx(gpu, c, c["T"])
+    x = to_dev_bf16(d["x"])
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    bufs, h = gpu.DispatchBuffers(ctx), gpu.Handle(ctx)
+    n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
+    y = torch.empty((n_cap, c["H"]), dtype=torch.bfloat16, device=dev())
+    y.view(torch.int16).fill_(0x3F80)
+    bufs.recv_rows.fill_(0)              # unrouted slots are never written: start both runs equal
+    bufs.recv_scales.fill_(0)
+    gpu.moe_dispatch(ctx, x, idx, bufs=bufs, handle=h)
+    ref_rows = bufs.recv_rows.clone()
+    ref_scales = bufs.recv_scales.clone()
+    ref_pos = h.pos.clone()
+    out_ref = gpu.moe_combine(ctx, y, w, h)
+    bufs.recv_rows.fill_(0)
+    bufs.recv_scales.fill_(0)
+    h.pos.fill_(-5)
+    out = torch.empty_like(out_ref)
+    pd = gpu.prepare_dispatch(ctx, x, idx, False, bufs, h)
+    pc = gpu.prepare_combine(ctx, y, w, h, out, c["T"])
+    pd()
+    pc()
+    torch.cuda.synchronize()
+    assert torch.equal(h.pos, ref_pos)
+    assert torch.equal(bufs.recv_rows, ref_rows)
+    assert torch.equal(bufs.recv_scales.view(torch.int32), ref_scales.view(torch.int32))
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16))
+    st, _ = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK
+    ctx.close()
