@@ -141,3 +141,18 @@ def test_product_does_not_reference_oracle():
                 assert "orc_" not in text, f
     nm = subprocess.run(["nm", "-D", moe.LIB_PATH], capture_output=True, text=True, check=True).stdout
     assert "orc_" not in nm
+
+
+@pytest.mark.gpu
+def test_c_consumer_runs():
+    """tests/c_abi_check (built by __graft_entry__.build()) drives layout,
+    dispatch and combine through the C ABI with no Python in between and checks
+    closed-form properties (counts, receive rows, identity round trip)."""
+    exe = os.path.join(ROOT, "tests", "c_abi_check")
+    if not os.path.exists(exe):
+        pytest.fail("tests/c_abi_check is not built (run __graft_entry__.build())")
+    print("running", exe, flush=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "result ok" in r.stdout
