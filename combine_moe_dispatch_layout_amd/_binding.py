@@ -175,7 +175,11 @@ class Context:
             pass
 
     def hint(self, kind):
-        return moe_size_hint(self.cfg, kind)
+        """moe_size_hint for this context's configuration (fixed, so cached)."""
+        cache = self.__dict__.setdefault("_hints", {})
+        if kind not in cache:
+            cache[kind] = moe_size_hint(self.cfg, kind)
+        return cache[kind]
 
     def tune(self, dispatch_chunks=0, combine_chunks=0):
         _check(load_library().moe_ctx_tune(self.handle, dispatch_chunks, combine_chunks), "moe_ctx_tune")
