@@ -110,8 +110,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Work split of a row-streaming kernel: each wavefront handles `chunks`
 // 16-byte chunks per lane of one token row (a "slice"), at most `cap`.  Rows
 // are cut into more slices when there are too few tokens to keep ~8
-// wavefronts per CU in flight.  Measured on MI355X: dispatch is fastest with
-// whole rows per wavefront (cap 16), combine with short slices (cap 2).
+// wavefronts per CU in flight.  Measured on MI355X: with its non-temporal
+// row stores the dispatch is fastest with one chunk per lane (5-11% ahead of
+// whole rows per wavefront on the prefill, grouped and skewed shapes), the
+// combine with two.
 void row_split(int64_t T, int64_t nchunk, int forced, int cap, int* chunks, int* nslices) {
     int c;
     if (forced > 0) {
@@ -477,7 +479,7 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     a.h_recv_counts = handle->recv_counts;
     a.err = ctx->err();
     int chunks, nslices;
-    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, 16, &chunks, &nslices);
+    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, 1, &chunks, &nslices);
     a.nslices = nslices;
     // at least one block so that the handle's offsets and counts are written for T = 0
     PackArgs a0 = a;
