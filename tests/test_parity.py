@@ -564,3 +564,16 @@ def test_prepared_calls_match(gpu):
     st, _ = gpu.moe_poll_error(ctx)
     assert st == gpu.MOE_OK
     ctx.close()
+
+
+@pytest.mark.parametrize("quant", [W.QUANT_BF16, W.QUANT_FP8])
+def test_many_tiles(gpu, quant):
+    """65,536 tokens: 256 layout tiles (per-tile prefixes over many tiles, the
+    arrival counter and the last block's scan), narrow rows to keep it quick."""
+    T = 65536
+    c = dict(index=21, T=T, H=128, E=256, R=32, k=8, quant=quant, layout=W.LAYOUT_CONTIGUOUS, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(65536 + quant))
+    idx = W.with_empty_slots(W.route_uniform(rng, T, c["E"], c["k"]), 0.05, seed=9)
+    x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, T, c["k"])
+    run_case(gpu, c, x, idx, w, max_tokens=T, tag="many-tiles-q%d" % quant)
