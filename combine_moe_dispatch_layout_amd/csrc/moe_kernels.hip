@@ -145,27 +145,34 @@ __device__ __forceinline__ int block_exclusive_scan(const int32_t* v, int32_t* o
     return total;
 }
 
+// The layout's tile is 256 tokens; 8 wavefronts of 32 tokens each keep every
+// wavefront's serial chain (one pass per 64-entry chunk) short.
+constexpr int kLayoutWaves = 8;
+constexpr int kLayoutThreads = 64 * kLayoutWaves;
+constexpr int kWaveTokens = kTileTokens / kLayoutWaves;
+
 template <int KMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
-    __shared__ unsigned long long peer_mask[kWavesPerBlock * MOE_MAX_EXPERTS];  // per chunk: lanes holding e
-    __shared__ unsigned long long rank_toks[kWavesPerBlock * MOE_MAX_RANKS];    // tokens of the wave sent to r
+__global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
+    __shared__ unsigned long long peer_mask[kLayoutWaves * MOE_MAX_EXPERTS];  // per chunk: lanes holding e
+    __shared__ unsigned long long rank_toks[kLayoutWaves * MOE_MAX_RANKS];    // tokens of the wave sent to r
     __shared__ unsigned long long tok_mask[kTileTokens];                       // ranks each token is sent to
-    __shared__ int32_t hist_e[kWavesPerBlock * MOE_MAX_EXPERTS];
-    __shared__ int32_t hist_r[kWavesPerBlock * MOE_MAX_RANKS];
+    __shared__ int32_t hist_e[kLayoutWaves * MOE_MAX_EXPERTS];
+    __shared__ int32_t hist_r[kLayoutWaves * MOE_MAX_RANKS];
     __shared__ int32_t tot[MOE_MAX_EXPERTS + MOE_MAX_RANKS];
     __shared__ int32_t off[MOE_MAX_EXPERTS + MOE_MAX_RANKS];
-    __shared__ int32_t wsum[kWavesPerBlock];
+    __shared__ int32_t wsum[kLayoutWaves];
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int E = a.E, R = a.R, k = a.k;
     const int ntiles = gridDim.x;
-    const int64_t tok0 = (int64_t)blockIdx.x * kTileTokens + w * 64;   // this wave's first token
-    const int64_t t = tok0 + lane;
-    const bool tok_ok = t < a.T;
-    const int64_t ntok = a.T - tok0 < 0 ? 0 : (a.T - tok0 > 64 ? 64 : a.T - tok0);
+    const int64_t tok0 = (int64_t)blockIdx.x * kTileTokens + w * kWaveTokens;   // this wave's first token
+    const int64_t t = tok0 + lane;          // lane = token of the wave (lanes < kWaveTokens)
+    const bool tok_ok = lane < kWaveTokens && t < a.T;
+    const int64_t ntok = a.T - tok0 < 0 ? 0 : (a.T - tok0 > kWaveTokens ? kWaveTokens : a.T - tok0);
     const int64_t nent = ntok * k;          // (token, slot) entries of this wave, row-major
+    const int nch = (kWaveTokens * k + 63) / 64;   // 64-entry chunks of a full wave
     const int64_t ent0 = tok0 * k;
     const uint64_t below = lanes_below(lane);
 
@@ -175,14 +182,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) {
         const int64_t i = (int64_t)c * 64 + lane;
-        raw[c] = c < k && i < nent ? a.topk_idx[ent0 + i] : -1;
+        raw[c] = c < nch && i < nent ? a.topk_idx[ent0 + i] : -1;
     }
-    for (int i = tid; i < kWavesPerBlock * E; i += kBlockThreads) {
+    for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) {
         peer_mask[i] = 0ull;
         hist_e[i] = 0;
     }
-    for (int i = tid; i < kWavesPerBlock * R; i += kBlockThreads) rank_toks[i] = 0ull;
-    tok_mask[tid] = 0ull;
+    for (int i = tid; i < kLayoutWaves * R; i += kLayoutThreads) rank_toks[i] = 0ull;
+    if (tid < kTileTokens) tok_mask[tid] = 0ull;
     int ev[KMAX];
     bool bad = false;
 #pragma unroll
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) {
         erl[c] = 0;
-        if (c < k) {
+        if (c < nch) {
             const int e = ev[c];
             unsigned long long* pm = &peer_mask[w * E + (e >= 0 ? e : 0)];
             if (e >= 0) {
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
                 const int r = div_magic(e, a.el_magic);
                 atomicOr(pm, 1ull << lane);
                 atomicOr(&rank_toks[w * R + r], 1ull << tl);
-                atomicOr(&tok_mask[w * 64 + tl], 1ull << r);
+                atomicOr(&tok_mask[w * kWaveTokens + tl], 1ull << r);
             }
             __builtin_amdgcn_wave_barrier();
             if (e >= 0) {
@@ -233,16 +240,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     // tile totals: kept in LDS for a single tile, else published (transposed
     // per-tile counts for the dispatch kernel's tile prefixes, plus atomic
     // grand totals for the last block)
-    for (int i = tid; i < kWavesPerBlock * R; i += kBlockThreads) hist_r[i] = __popcll(rank_toks[i]);
+    for (int i = tid; i < kLayoutWaves * R; i += kLayoutThreads) hist_r[i] = __popcll(rank_toks[i]);
     __syncthreads();
     int seen = 0;   // returned totals: using them makes the adds complete before the arrival below
-    for (int col = tid; col < E + R; col += kBlockThreads) {
+    for (int col = tid; col < E + R; col += kLayoutThreads) {
         const bool is_e = col < E;
         int32_t* h = is_e ? hist_e + col : hist_r + (col - E);
         const int stride = is_e ? E : R;
         int run = 0;
 #pragma unroll
-        for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+        for (int ww = 0; ww < kLayoutWaves; ++ww) {
             const int c = h[ww * stride];
             h[ww * stride] = run;
             run += c;
@@ -259,10 +266,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     // ---- phase 2: tile-local ranks out
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) {
-        if (c < k && ev[c] >= 0)
+        if (c < nch && ev[c] >= 0)
             a.erank[ent0 + (int64_t)c * 64 + lane] = (uint16_t)(hist_e[w * E + ev[c]] + erl[c]);
     }
-    const uint64_t rmask = tok_mask[w * 64 + lane];   // 0 for tokens past T
+    const uint64_t rmask = lane < kWaveTokens ? tok_mask[w * kWaveTokens + lane] : 0ull;   // 0 past T
     if (tok_ok) {
         for (uint64_t m = rmask; m != 0; m &= m - 1) {
             const int r = __ffsll((unsigned long long)m) - 1;
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
         if (tid == 0) s_last = (atomicAdd(a.done, 1u) == (unsigned)ntiles - 1);
         __syncthreads();
         if (!s_last) return;
-        for (int col = tid; col < E + R; col += kBlockThreads) {
+        for (int col = tid; col < E + R; col += kLayoutThreads) {
             tot[col] = __hip_atomic_load(&a.grand_tot[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             a.grand_tot[col] = 0;
         }
@@ -301,14 +308,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_layout(LayoutArgs a) {
     }
 
     // offsets: exclusive scans over experts and over ranks
-    const int total_e = block_exclusive_scan(tot, off, E, wsum);
-    const int total_r = block_exclusive_scan(tot + E, off + E, R, wsum);
-    for (int e = tid; e < E; e += kBlockThreads) {
+    const int total_e = block_exclusive_scan<kLayoutThreads>(tot, off, E, wsum);
+    const int total_r = block_exclusive_scan<kLayoutThreads>(tot + E, off + E, R, wsum);
+    for (int e = tid; e < E; e += kLayoutThreads) {
         a.eoff[e] = off[e];
         a.cnt_e[e] = tot[e];
         if (a.out_cnt_e != nullptr) a.out_cnt_e[e] = tot[e];
     }
-    for (int r = tid; r < R; r += kBlockThreads) {
+    for (int r = tid; r < R; r += kLayoutThreads) {
         a.roff[r] = off[E + r];
         a.cnt_r[r] = tot[E + r];
         if (a.out_cnt_r != nullptr) a.out_cnt_r[r] = tot[E + r];
@@ -932,9 +939,9 @@ dim3 items_grid(int64_t items, int max_blocks) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s) {
-    if (a.k <= 8) hipLaunchKernelGGL(k_layout<8>, dim3(ntiles), dim3(kBlockThreads), 0, s, a);
-    else if (a.k <= 16) hipLaunchKernelGGL(k_layout<16>, dim3(ntiles), dim3(kBlockThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_layout<32>, dim3(ntiles), dim3(kBlockThreads), 0, s, a);
+    if (a.k <= 8) hipLaunchKernelGGL(k_layout<8>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
+    else if (a.k <= 16) hipLaunchKernelGGL(k_layout<16>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_layout<32>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
     return hipGetLastError();
 }
 
