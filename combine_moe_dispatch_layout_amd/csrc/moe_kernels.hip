@@ -4,7 +4,7 @@
 // topk_idx once, dispatch reads each token row once and writes it to every
 // destination, combine reads every expert-output row once and writes each
 // token row once.  Design points:
-//  * Layout: one block per 256-token tile, 4 wavefronts of 64 tokens.  Stable
+//  * Layout: one block per 256-token tile, 8 wavefronts of 32 tokens.  Stable
 //    (token, slot) ranks come from per-expert lane masks built with LDS ORs
 //    (the lanes holding one expert find each other) plus per-wavefront LDS
 //    histograms -- no atomic decides any order, so results are deterministic.
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     }
     __syncthreads();
 
-    // ---- per-wavefront rank counts; exclusive prefixes over the 4 wavefronts;
+    // ---- per-wavefront rank counts; exclusive prefixes over the wavefronts;
     // tile totals: kept in LDS for a single tile, else published (transposed
     // per-tile counts for the dispatch kernel's tile prefixes, plus atomic
     // grand totals for the last block)
