@@ -42,7 +42,7 @@ def _bind(path):
     lib.orc_layout.argtypes = [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.orc_positions.restype = _i64
     lib.orc_positions.argtypes = [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
-                                  _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp]
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]
     lib.orc_quant_rows.restype = None
     lib.orc_quant_rows.argtypes = [_vp, _i64, _i32, _vp, _vp]
     lib.orc_dispatch_rows.restype = None
@@ -124,16 +124,19 @@ def positions(topk_idx, num_experts, num_ranks, lay, max_tokens=0, src_rank=0):
     recv_src = np.empty(max(T * k, 1), np.int32)
     pos_ll = np.empty((T, k), np.int32) if max_tokens > 0 else None
     n_pairs = ctypes.c_int64(0)
+    overflow = ctypes.c_int64(0)
     n_send = _load().orc_positions(
         _p(idx), T, k, E, R, _p(lay["num_tokens_per_expert"]), _p(lay["num_tokens_per_rank"]),
         _p(lay["is_token_in_rank"]), _p(eoff), _p(roff), _p(pos), _p(spos),
-        _p(send_src), _p(recv_src), max_tokens, src_rank, _p(pos_ll), ctypes.byref(n_pairs))
+        _p(send_src), _p(recv_src), max_tokens, src_rank, _p(pos_ll), ctypes.byref(n_pairs),
+        ctypes.byref(overflow))
     if n_send < 0:
         raise MemoryError("oracle positions: out of host memory")
     n_pairs = n_pairs.value
     return {"expert_offsets": eoff, "rank_offsets": roff, "pos": pos, "spos": spos,
             "send_src_idx": send_src[:n_send].copy(), "recv_src_idx": recv_src[:n_pairs].copy(),
-            "pos_ll": pos_ll, "n_send": int(n_send), "n_pairs": int(n_pairs)}
+            "pos_ll": pos_ll, "n_send": int(n_send), "n_pairs": int(n_pairs),
+            "ll_overflow": int(overflow.value)}
 
 
 def quant_rows(x_bf16):

@@ -177,7 +177,10 @@ int64_t orc_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R,
  * "Performance tuning").  The slot of (t, j) is s0*M + (its rank among the
  * rows for expert e), and pos_ll[t, j] = e * cap + slot indexes the padded
  * buffer viewed as [E, cap, row] (rank-major then local-expert, because
- * e = r * El + local).  Requires T <= M (checked by the caller).
+ * e = r * El + local).  The caller ensures T <= M; a row whose rank among
+ * expert e's rows is M or more (only possible when a token repeats an
+ * expert) has no slot: pos_ll = -1 (it is not placed), and *ll_overflow
+ * counts such rows.  The other outputs describe the routing and do not change.
  * Returns N_send (the number of send rows), or -1 if out of host memory;
  * *n_pairs gets N_pairs. */
 int64_t orc_positions(const int64_t* topk_idx, int64_t T, int k, int E, int R,
@@ -187,7 +190,8 @@ int64_t orc_positions(const int64_t* topk_idx, int64_t T, int k, int E, int R,
                       int32_t* expert_offsets, int32_t* rank_offsets,
                       int32_t* pos, int32_t* spos,
                       int32_t* send_src, int32_t* recv_src,
-                      int64_t M, int s0, int32_t* pos_ll, int64_t* n_pairs)
+                      int64_t M, int s0, int32_t* pos_ll, int64_t* n_pairs,
+                      int64_t* ll_overflow)
 {
     expert_offsets[0] = 0;
     for (int e = 0; e < E; e++) expert_offsets[e + 1] = expert_offsets[e] + num_tokens_per_expert[e];
@@ -198,6 +202,7 @@ int64_t orc_positions(const int64_t* topk_idx, int64_t T, int k, int E, int R,
     int32_t* cr = (int32_t*)calloc((size_t)R, sizeof(int32_t));   /* running per-rank counters */
     if (ce == NULL || cr == NULL) { free(ce); free(cr); return -1; }
     int64_t cap = M * (int64_t)R;
+    int64_t overflow = 0;
 
     for (int64_t t = 0; t < T; t++) {
         for (int j = 0; j < k; j++) {
@@ -207,7 +212,15 @@ int64_t orc_positions(const int64_t* topk_idx, int64_t T, int k, int E, int R,
                 int32_t rank_in_expert = ce[e]++;
                 p = expert_offsets[e] + rank_in_expert;
                 recv_src[p] = (int32_t)t;
-                if (M > 0) pl = (int32_t)(e * cap + (int64_t)s0 * M + rank_in_expert);
+                /* low latency: this source's window of expert e holds M slots
+                   (fixed-size buffers of num_max_dispatch_tokens_per_rank rows);
+                   a row past it is not placed.  With distinct experts per token
+                   and T <= M this cannot happen; a token that repeats an expert
+                   can make it happen. */
+                if (M > 0) {
+                    if (rank_in_expert < M) pl = (int32_t)(e * cap + (int64_t)s0 * M + rank_in_expert);
+                    else overflow++;
+                }
             }
             pos[t * k + j] = p;
             if (M > 0) pos_ll[t * k + j] = pl;
@@ -224,6 +237,7 @@ int64_t orc_positions(const int64_t* topk_idx, int64_t T, int k, int E, int R,
     free(ce);
     free(cr);
     *n_pairs = expert_offsets[E];
+    if (ll_overflow) *ll_overflow = overflow;
     return rank_offsets[R];
 }
 

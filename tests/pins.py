@@ -215,14 +215,32 @@ def check_layout_and_positions(orc, idx, E, R, M=0, s0=0):
         cap = M * R
         pl = pp["pos_ll"].ravel()
         v = pos_ref >= 0
-        e = flat[v]
-        slot = pl[v] - e * cap
-        # slots of one expert: this source's window [s0*M, s0*M + M), dense, in token order
         assert np.all(pl[~v] == -1)
-        for ex in np.unique(e):
-            s = slot[e == ex]
-            assert np.array_equal(s, s0 * M + np.arange(s.size)), "LL slots"
+        # slots of one expert: this source's window [s0*M, s0*M + M), dense, in
+        # (token, slot) order; rows past the window's M slots are not placed
+        vi = np.flatnonzero(v)
+        over = 0
+        for ex in np.unique(flat[vi]):
+            sel = vi[flat[vi] == ex]
+            placed = min(sel.size, M)
+            assert np.array_equal(pl[sel[:placed]] - ex * cap, s0 * M + np.arange(placed)), "LL slots"
+            assert np.all(pl[sel[placed:]] == -1), "rows past the window must not be placed"
+            over += sel.size - placed
+        assert pp["ll_overflow"] == over, "LL overflow count"
     return lay, pp
+
+
+def repeated_expert_routing(T, k, E, rng):
+    """Every token repeats expert 0 in two of its slots: expert 0 then receives
+    2T rows from one source, past a window of M = T slots."""
+    idx = route_distinct(rng, T, E, k)
+    idx[:, 1] = 0
+    idx[:, 0] = 0
+    return idx
+
+
+def route_distinct(rng, T, E, k):
+    return np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
 
 
 def brute_tiny(idx, E, R):

@@ -36,6 +36,7 @@ MUTANTS = [
     ("send_order_reversed", "sp = rank_offsets[r] + cr[r]++;",
      "sp = rank_offsets[r + 1] - 1 - cr[r]++;"),
     ("ll_slot_without_source", "(int64_t)s0 * M + rank_in_expert", "rank_in_expert"),
+    ("ll_window_ignored", "if (rank_in_expert < M) pl =", "if (rank_in_expert < M + 1000000) pl ="),
     ("quant_scale_swapped", "float s = 448.0f / ap;", "float s = ap / 448.0f;"),
     ("quant_no_floor", "float ap = a > 1e-4f ? a : 1e-4f;", "float ap = a;"),
     ("quant_amax_signed", "float v = fabsf(orc_bf16_to_f32(x[b * 128 + i]));",
@@ -107,6 +108,7 @@ def run_all_pins(orc):
     pins.check_layout_and_positions(orc, idx, 32, 4)
     pins.check_layout_and_positions(orc, W.with_empty_slots(idx, 0.25), 32, 4, M=80, s0=2)
     pins.check_tiny_brute(orc, W.make("tiny")["topk_idx"], 8, 2)
+    pins.check_layout_and_positions(orc, pins.repeated_expert_routing(40, 4, 8, rng), 8, 2, M=40, s0=1)
     f = np.zeros((3, 256), np.float32)
     f[1] = np.linspace(-3, 1, 256)
     f[2] = np.exp2(np.arange(256) % 30 - 25.0)

@@ -29,6 +29,19 @@ def test_layout_positions_random(orc, T, k, E, R):
     pins.check_layout_and_positions(orc, idx, E, R, M=max(T, 1) + 5, s0=R - 1)
 
 
+def test_ll_window_overflow(orc):
+    """A token that repeats an expert can send one expert more rows than the
+    window of M slots; the rows past it are not placed and are counted."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    T, k, E, R = 40, 4, 8, 2
+    idx = pins.repeated_expert_routing(T, k, E, rng)
+    _, pp = pins.check_layout_and_positions(orc, idx, E, R, M=T, s0=1)
+    assert pp["ll_overflow"] > 0
+    # distinct experts per token and T <= M: never an overflow
+    _, pp = pins.check_layout_and_positions(orc, pins.route_distinct(rng, T, E, k), E, R, M=T, s0=1)
+    assert pp["ll_overflow"] == 0
+
+
 def test_layout_degenerate(orc):
     # every slot to one expert; duplicates inside a row; bad ids; all empty
     T, k, E, R = 50, 4, 16, 4
