@@ -435,6 +435,6 @@ def moe_poll_error(ctx):
     """Synchronizes the current stream; returns (status, raw flags) and clears them."""
     flags = ctypes.c_uint32(0)
     st = load_library().moe_poll_error(ctx.handle, _stream(), ctypes.byref(flags))
-    if st not in (MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_DEVICE_BOUNDS):
+    if st not in (MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY, MOE_ERR_DEVICE_BOUNDS):
         raise MoeError(st, "moe_poll_error")
     return st, flags.value

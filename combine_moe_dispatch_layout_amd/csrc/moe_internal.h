@@ -24,6 +24,7 @@ constexpr int bwd_max_waves(int k) { return k > 8 ? 4 : 16; }
 // Bits of the sticky device error word.
 constexpr uint32_t kErrBadTopk = 1u;
 constexpr uint32_t kErrBounds = 2u;
+constexpr uint32_t kErrCapacity = 4u;   // a low-latency slot window overflowed (row not placed)
 
 struct LayoutArgs {
     const int64_t* topk_idx;   // [T, k]

@@ -456,10 +456,15 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
         cpos = a.eoff[e] + in_expert;
         int64_t row = cpos;
         if (LL) row = (int64_t)e * a.cap + (int64_t)a.s0 * a.max_tokens + in_expert;
-        if (cpos < 0 || cpos >= a.pairs_cap || row < 0 || row >= a.recv_cap_rows ||
-            (LL && in_expert >= a.max_tokens)) {
+        if (cpos < 0 || cpos >= a.pairs_cap) {
             atomicOr(a.err, kErrBounds);
             cpos = -1;
+        } else if (LL && in_expert >= a.max_tokens) {
+            // past this source's window of the expert (possible only when a
+            // token repeats an expert): the row is not placed
+            atomicOr(a.err, kErrCapacity);
+        } else if (row < 0 || row >= a.recv_cap_rows) {
+            atomicOr(a.err, kErrBounds);
         } else {
             rrow = (int)row;
         }
@@ -671,13 +676,20 @@ __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
     int rrow = -1;
     if (e >= 0) {
         const int64_t row = (int64_t)e * a.cap + (int64_t)a.s0 * a.max_tokens + rank;
-        if (rank >= a.max_tokens || row >= a.recv_cap_rows) atomicOr(a.err, kErrBounds);
-        else rrow = (int)row;
+        if (rank >= a.max_tokens) {
+            // past this source's window of the expert (only when a token repeats
+            // an expert): the row is not placed
+            if (s == 0) atomicOr(a.err, kErrCapacity);
+        } else if (row >= a.recv_cap_rows) {
+            atomicOr(a.err, kErrBounds);
+        } else {
+            rrow = (int)row;
+        }
     }
     if (s == 0 && lane < k) {
         a.h_pos[(int64_t)t * k + lane] = rrow;
         const int64_t cp = (int64_t)lessv + rank;   // expert-major position
-        if (rrow >= 0 && cp < a.pairs_cap) a.h_recv_src[cp] = t;
+        if (e >= 0 && cp < a.pairs_cap) a.h_recv_src[cp] = t;
     }
 
     // ---- copy (and quantise) the slice into the token's slots

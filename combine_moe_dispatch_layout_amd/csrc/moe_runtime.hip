@@ -625,6 +625,7 @@ MOE_API moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags) {
     if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
     if (flags) *flags = v;
     if (v & kErrBadTopk) return MOE_ERR_BAD_TOPK;
+    if (v & kErrCapacity) return MOE_ERR_CAPACITY;
     if (v & kErrBounds) return MOE_ERR_DEVICE_BOUNDS;
     return MOE_OK;
 }

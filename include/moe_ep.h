@@ -60,7 +60,9 @@ typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, wrong device, bad config value */
     MOE_ERR_UNSUPPORTED = 2,   /* outside the supported limits below */
-    MOE_ERR_CAPACITY = 3,      /* num_tokens > max_tokens (low-latency: > capacity per source rank) */
+    MOE_ERR_CAPACITY = 3,      /* num_tokens > max_tokens (low-latency: > capacity per source rank);
+                                  also from moe_poll_error: a low-latency slot window overflowed
+                                  (a token repeated an expert), the rows past it were not placed */
     MOE_ERR_HANDLE = 4,        /* handle not produced by moe_dispatch on a compatible context */
     MOE_ERR_HIP = 5,           /* a HIP runtime call failed */
     MOE_ERR_BAD_TOPK = 6,      /* from moe_poll_error: an expert id outside [-1, E) was seen */
@@ -177,7 +179,10 @@ moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t nu
  *   recv:  CONTIGUOUS: expert-major, rows [expert_offsets[e], expert_offsets[e+1])
  *          for expert e, ordered by (token, slot);
  *          PADDED_LL: row e*cap + s0*M + i (cap = M*R) holds the i-th token
- *          routed to expert e; other slots are never written.
+ *          routed to expert e, for i < M; other slots are never written.  A
+ *          row with i >= M (possible only when a token repeats an expert)
+ *          is not placed: its pos is -1 and moe_poll_error reports
+ *          MOE_ERR_CAPACITY.
  * Scales (fp8 only) are fp32 [rows, H/128], row-parallel to the data rows. */
 typedef struct moe_dispatch_buffers {
     void*  send_rows;     /* CONTIGUOUS: required; PADDED_LL: must be NULL */
@@ -190,7 +195,7 @@ typedef struct moe_dispatch_buffers {
  * of caller-owned device buffers, sized by the MOE_BUF_HANDLE_* hints).
  *   pos[t, j]        row of slot j of token t in the receive layout
  *                    (CONTIGUOUS: expert-major row; PADDED_LL: e*cap + slot),
- *                    -1 for an empty slot
+ *                    -1 for an empty slot or a row that was not placed
  *   expert_offsets   exclusive prefix sum of the per-expert counts (E+1)
  *   rank_offsets     exclusive prefix sum of the per-rank token counts (R+1)
  *   send_src_idx[i]  token of send row i (rank_offsets[R] entries)
@@ -307,8 +312,10 @@ moe_status moe_hook_wait(const moe_hook* hook, void* stream);
 
 /* ---------------------------------------------------------------- errors */
 /* Synchronize `stream`, read and clear the sticky device error word.
- * Returns MOE_OK, MOE_ERR_BAD_TOPK or MOE_ERR_DEVICE_BOUNDS (the first set,
- * in that order); *flags (host, may be NULL) receives the raw bits. */
+ * Returns MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY or MOE_ERR_DEVICE_BOUNDS
+ * (the first set, in that order); *flags (host, may be NULL) receives the raw
+ * bits (1: bad expert id, 2: row outside its buffer, 4: low-latency window
+ * overflow). */
 moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags);
 
 /* ---------------------------------------------------------------- timing */

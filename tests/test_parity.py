@@ -96,7 +96,12 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     else:
         gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=reuse, bufs=bufs, handle=h)
     st, flags = gpu.moe_poll_error(ctx)
-    assert st == (gpu.MOE_ERR_BAD_TOPK if ref["bad_ids"] else gpu.MOE_OK), (st, flags)
+    want = gpu.MOE_OK
+    if ref["bad_ids"]:
+        want = gpu.MOE_ERR_BAD_TOPK
+    elif ll and ref["ll_overflow"]:
+        want = gpu.MOE_ERR_CAPACITY          # rows past a slot window are not placed
+    assert st == want, (st, flags)
 
     assert np.array_equal(bits_of(cnt_e), ref["num_tokens_per_expert"]), "num_tokens_per_expert"
     assert np.array_equal(bits_of(cnt_r), ref["num_tokens_per_rank"]), "num_tokens_per_rank"
@@ -111,8 +116,10 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     if not ll:
         assert np.array_equal(bits_of(h.send_src_idx[:n_send]), ref["send_src_idx"]), "send_src_idx"
 
-    # ---- payload rows
-    valid = ref["pos"] >= 0
+    # ---- payload rows (low latency: the rows that were placed)
+    valid = (pos_ref >= 0) & (ref["pos"] >= 0)
+    pos_eff = np.where(valid, ref["pos"], -1).astype(np.int32)   # expert-major row of each placed slot
+    n_placed = int(valid.sum())
     rowdt = np.uint8 if fp8 else np.uint16
     if ll:
         dst = torch.from_numpy(pos_ref[valid].astype(np.int64)).to(dev())
@@ -128,7 +135,7 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
             for e0 in range(0, c["E"], 16):
                 blk = rows[e0:e0 + 16]
                 written += int((blk[:, :, :64] != POISON).any(dim=2).sum())
-            assert written == n_pairs, ("LL slots written", written, n_pairs)
+            assert written == n_placed, ("LL slots written", written, n_placed)
     else:
         got = bits_of(bufs.recv_rows[:n_pairs]).view(rowdt)
         assert np.array_equal(got, ref["recv_rows"]), "expert-major receive rows"
@@ -156,7 +163,7 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     out = gpu.moe_combine(ctx, y, w_d, h)
     st, flags = gpu.moe_poll_error(ctx)
     assert st == gpu.MOE_OK, (st, flags)
-    out_ref = oracle.combine(yv, w, ref["pos"])
+    out_ref = oracle.combine(yv, w, pos_eff)
     got = bits_of(out)
     d = np.abs(pins.bf16_ordered(got) - pins.bf16_ordered(out_ref))
     n_diff = int((d != 0).sum())
@@ -577,3 +584,20 @@ def test_many_tiles(gpu, quant):
     x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
     w = W.softmax_weights(rng, T, c["k"])
     run_case(gpu, c, x, idx, w, max_tokens=T, tag="many-tiles-q%d" % quant)
+
+
+@pytest.mark.parametrize("T,reuse,quant", [(128, False, W.QUANT_FP8), (128, True, W.QUANT_BF16),
+                                           (600, False, W.QUANT_FP8), (600, True, W.QUANT_BF16)])
+def test_ll_window_overflow(gpu, T, reuse, quant):
+    """Every token repeats expert 0 in two slots, so expert 0 gets 2T rows from
+    this source against a window of M = T slots: the rows past the window are
+    not placed (pos -1), MOE_ERR_CAPACITY is reported, everything else matches
+    the oracle -- fused path (T = 128) and layout + pack path (T = 600, or a
+    reused layout)."""
+    c = dict(index=31, T=T, H=512, E=64, R=8, k=8, quant=quant, layout=W.LAYOUT_PADDED_LL, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(T + quant))
+    idx = pins.repeated_expert_routing(T, c["k"], c["E"], rng)
+    x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, T, c["k"])
+    ref = run_case(gpu, c, x, idx, w, reuse=reuse, max_tokens=T, src_rank=3, tag="ll-overflow")
+    assert ref["ll_overflow"] >= T          # 2T repeated rows, plus any other slot on expert 0

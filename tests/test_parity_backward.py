@@ -76,8 +76,10 @@ def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", rep
     ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"], max_tokens=M if ll else 0,
                           src_rank=src_rank, with_send=not ll)
     n_pairs = ref["n_pairs"]
-    pos = ref["pos"]                                     # expert-major row of each slot
     dst_np = ref["pos_ll"] if ll else ref["pos"]         # row in the GPU receive layout
+    # expert-major row of each slot that was placed (low latency: rows past a
+    # slot window are not placed and take no part in the backward either)
+    pos = np.where(dst_np >= 0, ref["pos"], -1).astype(np.int32)
     valid = pos >= 0
 
     x = to_dev_bf16(x_bits) if T else torch.empty((0, H), dtype=torch.bfloat16, device=dev())
@@ -87,7 +89,7 @@ def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", rep
     h = gpu.Handle(ctx)
     gpu.moe_dispatch(ctx, x, idx_d, reuse_layout=False, bufs=bufs, handle=h)
     st, flags = gpu.moe_poll_error(ctx)
-    assert st in (gpu.MOE_OK, gpu.MOE_ERR_BAD_TOPK), (st, flags)
+    assert st in (gpu.MOE_OK, gpu.MOE_ERR_BAD_TOPK, gpu.MOE_ERR_CAPACITY), (st, flags)
     assert np.array_equal(bits_of(h.pos[:T]), dst_np), "handle pos"
     del bufs
 
@@ -142,7 +144,7 @@ def run_backward(gpu, c, x_bits, idx, w, max_tokens=None, tune=None, tag="", rep
         for r0 in range(0, n_cap, 1 << 16):
             blk = gy[r0:r0 + (1 << 16)].view(torch.int16)
             touched += int((blk[:, :8] != GPOISON).any(dim=1).sum())
-        assert touched == n_pairs, ("grad_expert_out rows written", touched, n_pairs)
+        assert touched == int(valid.sum()), ("grad_expert_out rows written", touched, int(valid.sum()))
         gwh = bits_of(gw[:T]).astype(np.float64)
         err = np.abs(gwh - gw_ref)
         assert np.all(gwh[~valid] == 0.0), "empty slot -> grad_w = 0"
