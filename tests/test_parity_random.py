@@ -1,7 +1,7 @@
 """GPU parity over seeded random configurations: expert and rank counts,
 top-k, hidden size, token count, quantisation, layout, layout reuse, source
-rank and workgroup cap drawn together, with empty slots and repeated experts
-in a row, forward (layout, dispatch, combine) and backward (dispatch backward,
+rank and workgroup cap drawn together, with empty slots, repeated experts in
+a row and bad expert ids, forward (layout, dispatch, combine) and backward (dispatch backward,
 combine backward) against the oracle.  Same bar as the targeted tests."""
 import numpy as np
 import pytest
@@ -37,7 +37,7 @@ def _cases():
         out.append(dict(index=100 + len(out), T=T, H=H, E=E, R=R, k=k, quant=quant, layout=layout,
                         max_tokens=M, reuse=bool(rng.integers(0, 2)), s0=int(rng.integers(0, R)),
                         max_wg=int(rng.choice([0, 0, 0, 3, 50])), empty=float(rng.choice([0.0, 0.1, 0.4])),
-                        dup=float(rng.choice([0.0, 0.2]))))
+                        dup=float(rng.choice([0.0, 0.2])), bad=bool(rng.random() < 0.25)))
     return out
 
 
@@ -53,6 +53,10 @@ def _inputs(c):
     if c["dup"] and k > 1 and T:
         rows = rng.random(T) < c["dup"]
         idx[rows, 1] = idx[rows, 0]                     # the same expert in two slots of a row
+    if c["bad"] and idx.size:                         # ids outside [-1, E): flagged, treated as empty
+        flat = idx.reshape(-1)
+        for v in (E + 5, -7, E):
+            flat[int(rng.integers(0, flat.size))] = v
     x = W.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
     return x, idx, w
