@@ -156,3 +156,15 @@ def test_c_consumer_runs():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "result ok" in r.stdout
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: a missing libmoe_ep.so is an error, never a silent CPU path."""
+    from combine_moe_dispatch_layout_amd import _binding as B
+    saved = B._lib
+    B._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            B.load_library(str(tmp_path / "libmoe_ep.so"))
+    finally:
+        B._lib = saved
