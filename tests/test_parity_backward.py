@@ -279,6 +279,66 @@ def test_backward_consecutive_calls_shrinking(gpu):
     ctx.close()
 
 
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_two_live_handles(gpu, name):
+    """Handles are caller-owned storage: two dispatches on one context leave two
+    live handles, and the first one still drives combine and both backward
+    calls correctly after the second dispatch (micro-batches whose backward
+    runs in reverse order)."""
+    c = small_cfg(name, H=1024)
+    ll = c["layout"] == W.LAYOUT_PADDED_LL
+    H, k, M = c["H"], c["k"], 128
+    ctx = gpu.Context(gpu.make_config(M, H, c["E"], c["R"], k, 0, c["quant"], c["layout"]))
+    n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * H)
+    batches = []
+    for b, T in enumerate((120, 57)):
+        d = W.make(name, T=T, extra_seed=b + 1)
+        x = np.ascontiguousarray(d["x"][:, :H])
+        ref = oracle.dispatch(x, d["topk_idx"], c["E"], c["R"], quant=c["quant"], max_tokens=M if ll else 0,
+                              with_send=not ll)
+        bufs, h = gpu.DispatchBuffers(ctx), gpu.Handle(ctx)
+        gpu.moe_dispatch(ctx, to_dev_bf16(x), torch.from_numpy(d["topk_idx"]).to(dev()), bufs=bufs, handle=h)
+        dst_np = ref["pos_ll"] if ll else ref["pos"]
+        valid = ref["pos"] >= 0
+        cfg_b = dict(c, extra_seed=b + 1)
+        batches.append(dict(T=T, w=d["topk_weights"], ref=ref, bufs=bufs, h=h, dst_np=dst_np, valid=valid,
+                            dst=torch.from_numpy(dst_np[valid].astype(np.int64)).to(dev()),
+                            yv=W.expert_outputs({"cfg": cfg_b}, ref["n_pairs"]),
+                            go=W.grad_rows({"cfg": cfg_b}, T),
+                            g=W.grad_rows({"cfg": dict(cfg_b, extra_seed=b + 11)}, ref["n_pairs"])))
+    st, flags = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK, (st, flags)
+
+    def receive_layout(bt, rows_bits):
+        buf = torch.empty((n_cap, H), dtype=torch.bfloat16, device=dev())
+        buf.view(torch.int16).fill_(0x7FC0)
+        buf[bt["dst"]] = to_dev_bf16(rows_bits[bt["ref"]["pos"][bt["valid"]]])
+        return buf
+
+    for b, bt in enumerate(batches):              # forward, the older handle first
+        log("two live handles (%s): forward of batch %d (T=%d)" % (name, b, bt["T"]))
+        assert np.array_equal(bits_of(bt["h"].pos[:bt["T"]]), bt["dst_np"]), "handle pos"
+        got = bits_of(bt["bufs"].recv_rows[bt["dst"]].view(torch.uint8))
+        assert np.array_equal(got, bt["ref"]["recv_rows"][bt["ref"]["pos"][bt["valid"]]].view(np.uint8))
+        out = gpu.moe_combine(ctx, receive_layout(bt, bt["yv"]), torch.from_numpy(bt["w"]).to(dev()), bt["h"])
+        assert np.array_equal(bits_of(out), oracle.combine(bt["yv"], bt["w"], bt["ref"]["pos"])), "combine"
+    for b in (1, 0):                              # backward, the newer handle first
+        bt = batches[b]
+        log("two live handles (%s): backward of batch %d" % (name, b))
+        pos = bt["ref"]["pos"]
+        gx = gpu.moe_dispatch_backward(ctx, receive_layout(bt, bt["g"]), bt["h"])
+        assert np.array_equal(bits_of(gx), oracle.dispatch_backward(bt["g"], pos)), "dispatch backward"
+        gy, gw = gpu.moe_combine_backward(ctx, to_dev_bf16(bt["go"]), torch.from_numpy(bt["w"]).to(dev()),
+                                          receive_layout(bt, bt["yv"]), bt["h"])
+        gy_ref, gw_ref = oracle.combine_backward(bt["go"], bt["w"], bt["yv"], pos)
+        assert np.array_equal(bits_of(gy[bt["dst"]]), gy_ref[pos[bt["valid"]]]), "combine backward rows"
+        err = np.abs(bits_of(gw).astype(np.float64) - gw_ref)
+        assert np.all(err <= grad_w_bound(bt["go"], bt["yv"], pos)), "grad_w outside the summation bound"
+    st, flags = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK, (st, flags)
+    ctx.close()
+
+
 def test_backward_api_errors(gpu):
     c = small_cfg("prefill")
     ctx = gpu.Context(gpu.make_config(64, c["H"], c["E"], c["R"], c["k"], 0, 0, 0))
