@@ -106,14 +106,27 @@ def step_bwd(moe, s):
                              grad_expert_out=s["grad_y"], grad_weights=s["grad_w"])
 
 
-def kernel_table(kt, alg):
+def percentiles_us(ms):
+    """p10, p50 and p90 of per-launch durations (ms) in microseconds."""
+    import numpy as np
+    return [round(float(v), 2) for v in np.percentile(1e3 * np.asarray(ms, dtype=np.float64), [10, 50, 90])]
+
+
+def kernel_table(kt, alg, cold=None):
+    """Per kernel: mean event duration and algorithmic GB/s, p10/p50/p90 of the
+    launches, and for each pass in `cold` ({label: timings}, passes with the
+    caches flushed between steps) the same percentiles."""
     out = {}
     for name, b in alg.items():
         n = kt[name]["launches"]
         if n == 0 or b == 0:
             continue
         us = 1e3 * kt[name]["total_ms"] / n
-        out[name] = {"us": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+        out[name] = {"us": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                     "us_p10_p50_p90": percentiles_us(kt[name]["ms"])}
+        for label, kc in (cold or {}).items():
+            if kc[name]["launches"]:
+                out[name]["us_%s_p10_p50_p90" % label] = percentiles_us(kc[name]["ms"])
     return out
 
 
@@ -219,15 +232,18 @@ def timed_kernels(moe, torch, s, steps, flush=None, fn=step):
     """Per-kernel durations from the HIP events the library records around
     each of its launches, on its launch stream, over `steps` more steps.  The
     events add a few microseconds per launch, so this pass is kept apart from
-    the wall-clock pass above.  With `flush`, a 1 GiB buffer is rewritten
-    between steps (outside the kernel events) so caches start cold."""
+    the wall-clock pass above.  With `flush` (a function), it runs before each
+    step, outside the kernel events, so that the caches start cold."""
     s["ctx"].timing_begin(3 * steps + 3)
     for _ in range(steps):
         if flush is not None:
-            flush.add_(1)
+            flush()
         fn(moe, s)
     torch.cuda.synchronize()
+    per = s["ctx"].timing_launches()
     kt = s["ctx"].timing_end()
+    for name in kt:
+        kt[name]["ms"] = [ms for n, ms in per if n == name]
     st, _ = moe.moe_poll_error(s["ctx"])
     assert st == moe.MOE_OK, st
     return kt
@@ -334,9 +350,10 @@ def copy_reference(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (us * 1e-6) / 1e9
 
 
-def all_configs(moe, W, torch, steps=50):
+def all_configs(moe, W, torch, flushes, steps=50):
     """Warm step time and algorithmic GB/s of every workload (the layout-reusing
-    step for the contiguous layout, the fused low-latency step for the padded one)."""
+    step for the contiguous layout, the fused low-latency step for the padded one),
+    and per kernel the p10/p50/p90 event durations warm and cold (caches flushed)."""
     out = {}
     for name in ("tiny", "decode", "prefill", "grouped", "skewed"):
         s = setup(moe, W, torch, name)
@@ -348,11 +365,14 @@ def all_configs(moe, W, torch, steps=50):
             fn = step_ll
             alg["layout"] = 0
         us = 1e6 * timed(moe, torch, s, steps, 10, fn=fn) / steps
+        kt = timed_kernels(moe, torch, s, steps, fn=fn)
+        kt_cold = {lb: timed_kernels(moe, torch, s, steps, flush=f, fn=fn) for lb, f in flushes.items()}
         b = sum(alg.values())
         out[name] = {"T": T, "H": c["H"], "E": c["E"], "R": c["R"], "k": c["k"],
                      "mode": ("fp8 " if c["quant"] else "bf16 ") + ("padded-LL" if c["layout"] else "send+contiguous"),
                      "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                     "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+                     "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                     "kernels": kernel_table(kt, alg, cold=kt_cold)}
         s["ctx"].close()
         del s
         torch.cuda.empty_cache()
@@ -435,7 +455,16 @@ def main():
     ms_per_step = 1e3 * wall / a.steps
     value = step_bytes / (wall / a.steps) / 1e9
 
-    per_kernel = kernel_table(kt, alg)
+    # the same steps with the caches flushed before each one by a 1 GiB buffer (4x the Infinity
+    # Cache): "cold" rewrites it (its dirty lines are written back during the step), "cold_read"
+    # only reads it (evicts without leaving dirty lines)
+    flushes = {}
+    if not a.profile_only:
+        fbuf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        flushes = {"cold": lambda: fbuf.add_(1), "cold_read": lambda: fbuf.sum()}
+    cold_pass = lambda fn_, steps_: {lb: timed_kernels(moe, torch, s, steps_, flush=f, fn=fn_)
+                                     for lb, f in flushes.items()}
+    per_kernel = kernel_table(kt, alg, cold=cold_pass(fn, min(a.steps, 100)))
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     achieved = per_kernel[dom]["GB/s"]
 
@@ -476,7 +505,7 @@ def main():
             "us_per_step": round(us_b, 2),
             "alg_bytes_per_step": sum(alg_b.values()),
             "GB/s": round(sum(alg_b.values()) / (us_b * 1e-6) / 1e9, 1),
-            "kernels": kernel_table(kt_b, alg_b),
+            "kernels": kernel_table(kt_b, alg_b, cold=cold_pass(step_bwd, min(a.steps, 100))),
             "traffic_bytes_per_launch": {k_: traffic_for(k_, a.workload + "_backward") for k_ in alg_b}}
         for key in ("grad_recv", "grad_out", "grad_x", "grad_y", "grad_w"):
             del s[key]
@@ -488,9 +517,9 @@ def main():
 
     if not a.profile_only and not a.no_decode and a.workload != "decode":
         sd = setup(moe, W, torch, "decode")
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > 256 MB MALL
         wall_d = timed(moe, torch, sd, 500, 50, fn=step_ll)
-        kt_d = timed_kernels(moe, torch, sd, 100, flush=flush, fn=step_ll)
+        kt_d = timed_kernels(moe, torch, sd, 100, flush=flushes["cold"], fn=step_ll)
+        kt_dr = timed_kernels(moe, torch, sd, 100, flush=flushes["cold_read"], fn=step_ll)
         alg_d = algorithmic_bytes(sd["c"], 128, 0, sd["n_pairs"], 128 * 8)
         ll_bytes = alg_d["dispatch"] + alg_d["combine"]      # routing is read inside dispatch
         warm_us = 1e6 * wall_d / 500
@@ -505,6 +534,8 @@ def main():
             pc()
         prep_us = 1e6 * timed(moe, torch, sd, 500, 50, fn=step_prepared) / 500
         cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("dispatch", "combine")}
+        cold_pct = {n: percentiles_us(kt_d[n]["ms"]) for n in ("dispatch", "combine")}
+        cold_read_pct = {n: percentiles_us(kt_dr[n]["ms"]) for n in ("dispatch", "combine")}
         line["decode"] = {
             "workload": "decode: T=128 H=7168 E=256 R=32 top-8 fp8 padded-LL",
             "step": "dispatch from topk_idx (one fused launch) + combine",
@@ -512,10 +543,12 @@ def main():
             "us_per_step_graph": round(graph_us, 2),
             "us_per_step_prepared_calls": round(prep_us, 2),
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
+            "us_per_kernel_cold_p10_p50_p90": cold_pct,
+            "us_per_kernel_cold_read_p10_p50_p90": cold_read_pct,
             "alg_bytes_per_step": ll_bytes,
             "GB/s_warm": round(ll_bytes / (warm_us * 1e-6) / 1e9, 1)}
         sd["ctx"].close()
-        del sd, flush
+        del sd
         torch.cuda.empty_cache()
 
     if not a.profile_only:
@@ -525,7 +558,7 @@ def main():
                                   "dominant_kernel_frac_of_copy": round(achieved / cp, 3)}
 
     if not a.profile_only and not a.no_configs and a.step == "forward":
-        line["configs"] = all_configs(moe, W, torch)
+        line["configs"] = all_configs(moe, W, torch, flushes)
 
     if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
         model, ncpu = host_cpu()

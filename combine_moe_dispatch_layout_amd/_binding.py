@@ -69,7 +69,8 @@ class moe_handle(ctypes.Structure):
 EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy", "moe_ctx_config",
            "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_backward",
            "moe_combine_backward", "moe_ctx_set_max_workgroups", "moe_hook_create", "moe_hook_destroy",
-           "moe_hook_record", "moe_hook_wait", "moe_poll_error", "moe_timing_begin", "moe_timing_end")
+           "moe_hook_record", "moe_hook_wait", "moe_poll_error", "moe_timing_begin", "moe_timing_end",
+           "moe_timing_launches")
 
 _lib = None
 
@@ -106,6 +107,8 @@ def load_library(path=LIB_PATH):
         "moe_poll_error": [vp, vp, u32p],
         "moe_timing_begin": [vp, i32],
         "moe_timing_end": [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+        "moe_timing_launches": [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float), i32,
+                                ctypes.POINTER(ctypes.c_int32)],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -190,6 +193,17 @@ class Context:
 
     def timing_begin(self, max_launches):
         _check(load_library().moe_timing_begin(self.handle, max_launches), "moe_timing_begin")
+
+    def timing_launches(self):
+        """[(kernel name, ms)] of every launch timed so far, in launch order
+        (before timing_end)."""
+        lib = load_library()
+        n = ctypes.c_int32(0)
+        _check(lib.moe_timing_launches(self.handle, None, None, 0, ctypes.byref(n)), "moe_timing_launches")
+        ids = (ctypes.c_int32 * max(n.value, 1))()
+        ms = (ctypes.c_float * max(n.value, 1))()
+        _check(lib.moe_timing_launches(self.handle, ids, ms, n.value, ctypes.byref(n)), "moe_timing_launches")
+        return [(KERNEL_NAMES[ids[i]], ms[i]) for i in range(n.value)]
 
     def timing_end(self):
         n = len(KERNEL_NAMES)

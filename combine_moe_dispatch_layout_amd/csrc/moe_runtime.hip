@@ -657,6 +657,24 @@ MOE_API moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches) {
     return MOE_OK;
 }
 
+MOE_API moe_status moe_timing_launches(moe_ctx* ctx, int32_t* kernel_ids, float* ms, int32_t capacity,
+                                       int32_t* count) {
+    if (ctx == nullptr || !ctx->timing || count == nullptr || capacity < 0 ||
+        (capacity > 0 && (kernel_ids == nullptr || ms == nullptr)))
+        return MOE_ERR_INVALID_ARG;
+    const int32_t n = (int32_t)ctx->kid.size();
+    *count = n;
+    for (int32_t i = 0; i < n && i < capacity; ++i) {
+        float v = 0.f;
+        if (hipEventSynchronize(ctx->ev1[i]) != hipSuccess ||
+            hipEventElapsedTime(&v, ctx->ev0[i], ctx->ev1[i]) != hipSuccess)
+            return MOE_ERR_HIP;
+        kernel_ids[i] = ctx->kid[i];
+        ms[i] = v;
+    }
+    return MOE_OK;
+}
+
 MOE_API moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches) {
     if (ctx == nullptr || !ctx->timing) return MOE_ERR_INVALID_ARG;
     moe_status st = MOE_OK;

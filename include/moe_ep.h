@@ -337,6 +337,16 @@ typedef enum moe_kernel_id {
 moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches);
 moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Per-launch durations of the timing window opened by moe_timing_begin, for
+ * percentiles (call before moe_timing_end, which frees the events).  Writes
+ * the kernel id (moe_kernel_id) and duration in milliseconds of the first
+ * min(capacity, count) timed launches, in launch order, into the host arrays
+ * kernel_ids and ms, and the number of timed launches into *count (host).
+ * Synchronizes on each launch's end event.  MOE_ERR_INVALID_ARG without an
+ * open timing window or with NULL arrays for capacity > 0. */
+moe_status moe_timing_launches(moe_ctx* ctx, int32_t* kernel_ids, float* ms, int32_t capacity,
+                               int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif

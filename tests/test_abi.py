@@ -128,6 +128,7 @@ def test_null_arguments_rejected(lib):
     assert lib.moe_poll_error(None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_begin(None, 4) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_end(None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_timing_launches(None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_product_does_not_reference_oracle():

@@ -363,10 +363,18 @@ def test_timing_api(gpu):
     for _ in range(3):
         gpu.moe_dispatch_layout(ctx, idx)
         gpu.moe_dispatch(ctx, x, idx, reuse_layout=True)
+    per = ctx.timing_launches()
+    assert [n for n, _ in per] == ["layout", "dispatch"] * 3, per
+    assert all(ms > 0 for _, ms in per)
     r = ctx.timing_end()
     assert r["layout"]["launches"] == 3 and r["dispatch"]["launches"] == 3
     assert r["combine"]["launches"] == 0
     assert r["dispatch"]["total_ms"] > 0
+    for name in ("layout", "dispatch"):   # per-launch durations add up to the totals
+        tot = sum(ms for n, ms in per if n == name)
+        assert abs(tot - r[name]["total_ms"]) <= 1e-6 * max(1.0, tot), (name, tot, r[name])
+    with pytest.raises(gpu.MoeError):     # no open timing window
+        ctx.timing_launches()
     ctx.close()
 
 
