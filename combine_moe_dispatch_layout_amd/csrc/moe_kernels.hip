@@ -714,6 +714,33 @@ __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
 }
 
 // ============================================================== combine
+// One output chunk (8 channels) from the KMAX row chunks in v: fp32 from +0,
+// w_j * y_j rounded, then added, slot by slot in ascending order; bf16 RNE.
+template <int KMAX>
+__device__ __forceinline__ u32x4 combine_chunk(const u32x4 (&v)[KMAX], const int* pj, const float* wj) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (pj[j] >= 0) {
+            const float wv = wj[j];
+            acc[0] = __fadd_rn(acc[0], __fmul_rn(wv, bf16_lo(v[j].x)));
+            acc[1] = __fadd_rn(acc[1], __fmul_rn(wv, bf16_hi(v[j].x)));
+            acc[2] = __fadd_rn(acc[2], __fmul_rn(wv, bf16_lo(v[j].y)));
+            acc[3] = __fadd_rn(acc[3], __fmul_rn(wv, bf16_hi(v[j].y)));
+            acc[4] = __fadd_rn(acc[4], __fmul_rn(wv, bf16_lo(v[j].z)));
+            acc[5] = __fadd_rn(acc[5], __fmul_rn(wv, bf16_hi(v[j].z)));
+            acc[6] = __fadd_rn(acc[6], __fmul_rn(wv, bf16_lo(v[j].w)));
+            acc[7] = __fadd_rn(acc[7], __fmul_rn(wv, bf16_hi(v[j].w)));
+        }
+    }
+    u32x4 o;
+    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    return o;
+}
+
 template <int C, int KMAX>
 __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item, int lane) {
     const int t = (int)(item / a.nslices);
@@ -742,8 +769,24 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
     const int64_t g0 = (int64_t)s * 64 * C + lane;
     const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.y);
     u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.out) + (int64_t)t * nchunk;
+    if (C * KMAX <= 16 && g0 - lane + C * 64 <= nchunk) {
+        // whole slice inside the row: every load of the slice is issued before
+        // any arithmetic, so that all C * k row chunks are in flight at once
+        // (chunk by chunk the wavefront waits for each chunk's rows in turn;
+        // measured on MI355X, ~1.5% slower on the prefill shape); at most 16
+        // chunks held, which keeps the kernel under 80 registers
+        u32x4 v[C][KMAX];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
+        for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                if (pj[j] >= 0) v[i][j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g0 + i * 64);
+#pragma unroll
+        for (int i = 0; i < C; ++i) __builtin_nontemporal_store(combine_chunk<KMAX>(v[i], pj, wj), out + g0 + i * 64);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {   // ragged tail of the row
         const int64_t g = g0 + i * 64;
         const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
         if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
@@ -751,27 +794,7 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
                 if (pj[j] >= 0) v[j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g);
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < KMAX; ++j) {
-                if (pj[j] >= 0) {
-                    const float wv = wj[j];
-                    acc[0] = __fadd_rn(acc[0], __fmul_rn(wv, bf16_lo(v[j].x)));
-                    acc[1] = __fadd_rn(acc[1], __fmul_rn(wv, bf16_hi(v[j].x)));
-                    acc[2] = __fadd_rn(acc[2], __fmul_rn(wv, bf16_lo(v[j].y)));
-                    acc[3] = __fadd_rn(acc[3], __fmul_rn(wv, bf16_hi(v[j].y)));
-                    acc[4] = __fadd_rn(acc[4], __fmul_rn(wv, bf16_lo(v[j].z)));
-                    acc[5] = __fadd_rn(acc[5], __fmul_rn(wv, bf16_hi(v[j].z)));
-                    acc[6] = __fadd_rn(acc[6], __fmul_rn(wv, bf16_lo(v[j].w)));
-                    acc[7] = __fadd_rn(acc[7], __fmul_rn(wv, bf16_hi(v[j].w)));
-                }
-            }
-            u32x4 o;
-            o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-            o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-            o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-            __builtin_nontemporal_store(o, out + g);
+            __builtin_nontemporal_store(combine_chunk<KMAX>(v, pj, wj), out + g);
         }
     }
 }
@@ -794,13 +817,46 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// One chunk (8 channels) of the output gradient gv against eight routed rows
+// v: grad_y rows get bf16(w_j * go), and dot[j] accumulates go * y_j (each
+// product of two bf16 values is exact in fp32, so the fused multiply-add
+// rounds as a separate add would).
+__device__ __forceinline__ void combine_bwd_chunk(const u32x4& gv, const u32x4 (&v)[8], const int* pj,
+                                                  const float* wj, float* dot, u32x4* gy, int64_t nchunk,
+                                                  int64_t g) {
+    const float gf[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
+                         bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (pj[j] >= 0) {
+            float d = dot[j];
+            d = __builtin_fmaf(gf[0], bf16_lo(v[j].x), d);
+            d = __builtin_fmaf(gf[1], bf16_hi(v[j].x), d);
+            d = __builtin_fmaf(gf[2], bf16_lo(v[j].y), d);
+            d = __builtin_fmaf(gf[3], bf16_hi(v[j].y), d);
+            d = __builtin_fmaf(gf[4], bf16_lo(v[j].z), d);
+            d = __builtin_fmaf(gf[5], bf16_hi(v[j].z), d);
+            d = __builtin_fmaf(gf[6], bf16_lo(v[j].w), d);
+            d = __builtin_fmaf(gf[7], bf16_hi(v[j].w), d);
+            dot[j] = d;
+            const float wv = wj[j];
+            u32x4 o;
+            o.x = f32_to_bf16(__fmul_rn(wv, gf[0])) | (f32_to_bf16(__fmul_rn(wv, gf[1])) << 16);
+            o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
+            o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
+            o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
+            __builtin_nontemporal_store(o, gy + (int64_t)pj[j] * nchunk + g);
+        }
+    }
+}
+
 // One block per token, one wavefront per row slice (blockDim.x / 64 slices of
 // C 16-byte chunks per lane).  For each chunk of the token's output gradient:
 // load it and the routed expert-output rows (eight slots at a time, to bound
-// registers), write bf16(w_j * go) to each routed row of grad_y, and
-// accumulate the chunk's products go * y_j into one fp32 partial dot product
-// per slot (a product of two bf16 values is exact in fp32, so a fused
-// multiply-add rounds exactly as a separate add would).  Partials are reduced
+// registers; with at most eight slots and the whole slice inside the row,
+// every load of the slice first), write bf16(w_j * go) to each routed row of
+// grad_y, and accumulate the chunk's products go * y_j into one fp32 partial
+// dot product per slot (combine_bwd_chunk).  Partials are reduced
 // over the wavefront (fixed butterfly), then over the block's wavefronts in
 // wavefront order through LDS: deterministic, and no device-scope fence (on
 // this chip a release fence writes back the L2, which costs more than the
@@ -839,43 +895,35 @@ __device__ __forceinline__ void combine_bwd_token(const CombineBwdArgs& a, int t
     float dot[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) dot[j] = 0.0f;
+    if (KMAX == 8 && C <= 2 && g0 - lane + C * 64 <= nchunk) {
+        // whole slice inside the row and at most eight slots: every load of the
+        // slice first, as in the combine (up to two chunks per lane: more would
+        // not fit the 128 registers of a 1024-thread block)
+        u32x4 gv[C], v[C][8];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int64_t g = g0 + i * 64;
-        const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
-        if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
-            const u32x4 gv = __builtin_nontemporal_load(go + g);
-            const float gf[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
-                                 bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+        for (int i = 0; i < C; ++i) gv[i] = __builtin_nontemporal_load(go + g0 + i * 64);
 #pragma unroll
-            for (int jb = 0; jb < KMAX; jb += 8) {
-                if (jb >= k) break;
-                u32x4 v[8];
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    if (pj[jb + jj] >= 0) v[jj] = __builtin_nontemporal_load(y + (int64_t)pj[jb + jj] * nchunk + g);
+            for (int i = 0; i < C; ++i)
+                if (pj[j] >= 0) v[i][j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g0 + i * 64);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int j = jb + jj;
-                    if (pj[j] >= 0) {
-                        float d = dot[j];
-                        d = __builtin_fmaf(gf[0], bf16_lo(v[jj].x), d);
-                        d = __builtin_fmaf(gf[1], bf16_hi(v[jj].x), d);
-                        d = __builtin_fmaf(gf[2], bf16_lo(v[jj].y), d);
-                        d = __builtin_fmaf(gf[3], bf16_hi(v[jj].y), d);
-                        d = __builtin_fmaf(gf[4], bf16_lo(v[jj].z), d);
-                        d = __builtin_fmaf(gf[5], bf16_hi(v[jj].z), d);
-                        d = __builtin_fmaf(gf[6], bf16_lo(v[jj].w), d);
-                        d = __builtin_fmaf(gf[7], bf16_hi(v[jj].w), d);
-                        dot[j] = d;
-                        const float wv = wj[j];
-                        u32x4 o;
-                        o.x = f32_to_bf16(__fmul_rn(wv, gf[0])) | (f32_to_bf16(__fmul_rn(wv, gf[1])) << 16);
-                        o.y = f32_to_bf16(__fmul_rn(wv, gf[2])) | (f32_to_bf16(__fmul_rn(wv, gf[3])) << 16);
-                        o.z = f32_to_bf16(__fmul_rn(wv, gf[4])) | (f32_to_bf16(__fmul_rn(wv, gf[5])) << 16);
-                        o.w = f32_to_bf16(__fmul_rn(wv, gf[6])) | (f32_to_bf16(__fmul_rn(wv, gf[7])) << 16);
-                        __builtin_nontemporal_store(o, gy + (int64_t)pj[j] * nchunk + g);
-                    }
+        for (int i = 0; i < C; ++i) combine_bwd_chunk(gv[i], v[i], pj, wj, dot, gy, nchunk, g0 + i * 64);
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t g = g0 + i * 64;
+            const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
+            if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
+                const u32x4 gv = __builtin_nontemporal_load(go + g);
+#pragma unroll
+                for (int jb = 0; jb < KMAX; jb += 8) {   // eight slots at a time
+                    if (jb >= k) break;
+                    u32x4 v[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        if (pj[jb + jj] >= 0) v[jj] = __builtin_nontemporal_load(y + (int64_t)pj[jb + jj] * nchunk + g);
+                    combine_bwd_chunk(gv, v, pj + jb, wj + jb, dot + jb, gy, nchunk, g);
                 }
             }
         }
