@@ -261,7 +261,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
             if (run != 0) seen |= atomicAdd(&a.grand_tot[col], run);
         }
     }
+    if (seen == -1) s_last = 2;   // never true: consumes the returned totals before the arrival
     __syncthreads();
+    // ---- arrival (see below), issued now so that its round trip overlaps phase 2
+    unsigned arrived = 0u;
+    if (ntiles > 1 && tid == 0) arrived = atomicAdd(a.done, 1u);
 
     // ---- phase 2: tile-local ranks out
 #pragma unroll
@@ -291,13 +295,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
 
     // ---- arrival: the last block reads (and resets) the grand totals.  Only
     // device-scope atomics cross blocks here (the totals, read back with atomic
-    // loads, and the arrival counter); each block's adds have completed before
-    // it arrives, so no memory fence is needed -- on this chip a device-scope
-    // release fence writes back the whole L2.
+    // loads, and the arrival counter); each block's adds have completed (their
+    // returned values were consumed before the barrier ahead of its arrival),
+    // so no memory fence is needed -- on this chip a device-scope release fence
+    // writes back the whole L2.
     if (ntiles > 1) {
-        if (seen == -1) s_last = 2;   // never true: consumes the returned totals
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(a.done, 1u) == (unsigned)ntiles - 1);
+        if (tid == 0) s_last = (arrived == (unsigned)ntiles - 1);
         __syncthreads();
         if (!s_last) return;
         for (int col = tid; col < E + R; col += kLayoutThreads) {
@@ -307,16 +310,18 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
         __syncthreads();
     }
 
-    // offsets: exclusive scans over experts and over ranks
-    const int total_e = block_exclusive_scan<kLayoutThreads>(tot, off, E, wsum);
-    const int total_r = block_exclusive_scan<kLayoutThreads>(tot + E, off + E, R, wsum);
+    // offsets: one exclusive scan over the expert counts followed by the rank
+    // counts; the rank offsets are the second part minus the expert total
+    const int total = block_exclusive_scan<kLayoutThreads>(tot, off, E + R, wsum);
+    const int total_e = off[E];
+    const int total_r = total - total_e;
     for (int e = tid; e < E; e += kLayoutThreads) {
         a.eoff[e] = off[e];
         a.cnt_e[e] = tot[e];
         if (a.out_cnt_e != nullptr) a.out_cnt_e[e] = tot[e];
     }
     for (int r = tid; r < R; r += kLayoutThreads) {
-        a.roff[r] = off[E + r];
+        a.roff[r] = off[E + r] - total_e;
         a.cnt_r[r] = tot[E + r];
         if (a.out_cnt_r != nullptr) a.out_cnt_r[r] = tot[E + r];
     }
