@@ -350,12 +350,15 @@ def copy_reference(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (us * 1e-6) / 1e9
 
 
-def all_configs(moe, W, torch, flushes, steps=50):
+def all_configs(moe, W, torch, flushes):
     """Warm step time and algorithmic GB/s of every workload (the layout-reusing
     step for the contiguous layout, the fused low-latency step for the padded one),
-    and per kernel the p10/p50/p90 event durations warm and cold (caches flushed)."""
+    and per kernel the p10/p50/p90 event durations warm and cold (caches flushed):
+    10 warm-up steps, then 1000 timed steps for the two latency-bound workloads
+    and 100 for the others."""
     out = {}
     for name in ("tiny", "decode", "prefill", "grouped", "skewed"):
+        steps = 1000 if name in ("tiny", "decode") else 100
         s = setup(moe, W, torch, name)
         c = s["c"]
         T = c["T"]
@@ -372,7 +375,7 @@ def all_configs(moe, W, torch, flushes, steps=50):
                      "mode": ("fp8 " if c["quant"] else "bf16 ") + ("padded-LL" if c["layout"] else "send+contiguous"),
                      "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                      "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                     "kernels": kernel_table(kt, alg, cold=kt_cold)}
+                     "steps": steps, "kernels": kernel_table(kt, alg, cold=kt_cold)}
         s["ctx"].close()
         del s
         torch.cuda.empty_cache()
