@@ -9,7 +9,8 @@
 //    (the lanes holding one expert find each other) plus per-wavefront LDS
 //    histograms -- no atomic decides any order, so results are deterministic.
 //    The last tile block to arrive (device-scope counter) scans the tile
-//    totals into global row bases, so count and scan are one launch.
+//    totals into global row bases, so count and scan are one launch; each
+//    block arrives before writing its in-tile ranks, overlapping the two.
 //  * Dispatch: one wavefront per (token, row slice).  The slice is loaded once
 //    into registers with 16-byte loads, optionally quantised to E4M3 in
 //    registers (block amax by cross-lane max over the 16 lanes holding one
@@ -21,9 +22,9 @@
 //    by 4% (prefill), 30% (fp8 grouped) and 10% (skewed) on its own, and cached
 //    stores would push ~0.9 GB per prefill launch through the 256 MB Infinity
 //    Cache, slowing a concurrent bf16 GEMM by 1.3x (its operands are evicted).
-//  * Combine: one wavefront per (token, row slice); for each 16-byte chunk the
-//    k routed rows are loaded together, accumulated in fp32 in slot order with
-//    separately rounded multiply and add, rounded once to bf16 (RNE).  The
+//  * Combine: one wavefront per (token, row slice); all k routed rows of the
+//    slice are loaded before any arithmetic, accumulated in fp32 in slot order
+//    with separately rounded multiply and add, rounded once to bf16 (RNE).  The
 //    expert outputs are read exactly once, so they use non-temporal loads
 //    (measured ~35% faster than cached loads here); short slices (2 chunks per
 //    lane) keep many small wavefronts in flight.
@@ -791,7 +792,7 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
         return;
     }
 #pragma unroll
-    for (int i = 0; i < C; ++i) {   // ragged tail of the row
+    for (int i = 0; i < C; ++i) {   // ragged row tail, or too many chunks to hold: chunk by chunk
         const int64_t g = g0 + i * 64;
         const ChunkState cs = chunk_state(g0 - lane + i * 64, nchunk);
         if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) {
