@@ -1,0 +1,82 @@
+"""Host logic of bench.py (CPU, no GPU): the single-GPU guard, and the
+algorithmic byte counts the roofline divides by, recomputed here from the sizes
+of the oracle's own outputs (every array the method must read or write, once)
+on seeded workloads."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "single GPU" in r.stderr
+    assert r.stdout == ""                      # no JSON line
+
+
+def _nbytes(*arrays):
+    return sum(a.nbytes for a in arrays if a is not None)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", 384), ("grouped", 384),
+                                    ("skewed", 384)])
+def test_algorithmic_bytes_match_the_oracle_outputs(name, T):
+    d = W.make(name, T=T)
+    c = d["cfg"]
+    T, H, E, R, k = c["T"], c["H"], c["E"], c["R"], c["k"]
+    ll = c["layout"] == W.LAYOUT_PADDED_LL
+    idx, w = d["topk_idx"], d["topk_weights"]
+    ref = oracle.dispatch(d["x"], idx, E, R, quant=c["quant"], max_tokens=c["max_tokens"] if ll else 0,
+                          with_send=not ll)
+    n_pairs, n_send = ref["n_pairs"], ref["n_send"]
+    got = bench.algorithmic_bytes(c, T, n_send, n_pairs, T * k)
+
+    # layout: the routing in; per-expert and per-rank counts and the token x rank flags out
+    assert got["layout"] == _nbytes(idx, ref["num_tokens_per_expert"], ref["num_tokens_per_rank"],
+                                    ref["is_token_in_rank"])
+    # dispatch: x and the routing in; every payload row (and scale row) out once, plus the
+    # handle: a position and a source index per routed slot, send sources, offsets and counts
+    pos_valid = ref["pos"][ref["pos"] >= 0]
+    handle = _nbytes(pos_valid, ref["recv_src_idx"], ref["expert_offsets"], ref["rank_offsets"],
+                     ref["num_tokens_per_expert"])
+    rows = _nbytes(ref["recv_rows"], ref["recv_scales"])
+    if not ll:
+        rows += _nbytes(ref["send_rows"], ref["send_scales"])
+        handle += _nbytes(ref["send_src_idx"])
+    assert got["dispatch"] == _nbytes(d["x"], idx) + rows + handle
+    # combine: each routed expert-output row (bf16) once, weights and positions per slot, the output
+    y_rows = 2 * H * n_pairs
+    assert got["combine"] == y_rows + _nbytes(w, ref["pos"]) + 2 * T * H
+    # backward: gradient rows mirror the forward's rows
+    b = bench.backward_bytes(c, T, n_pairs)
+    assert b["dispatch_bwd"] == y_rows + _nbytes(ref["pos"]) + 2 * T * H
+    assert b["combine_bwd"] == 2 * T * H + _nbytes(w, ref["pos"]) + 2 * y_rows + _nbytes(w)
+
+
+def test_percentiles_of_launch_durations():
+    ms = [0.001 * v for v in range(1, 101)]   # 1..100 us
+    p10, p50, p90 = bench.percentiles_us(ms)
+    assert p10 == pytest.approx(10.9) and p50 == pytest.approx(50.5) and p90 == pytest.approx(90.1)
+
+
+def test_kernel_table_reports_percentiles_and_cold_passes():
+    kt = {"dispatch": {"total_ms": 0.3, "launches": 3, "ms": [0.1, 0.1, 0.1]},
+          "combine": {"total_ms": 0.0, "launches": 0, "ms": []}}
+    cold = {"cold": {"dispatch": {"total_ms": 0.6, "launches": 3, "ms": [0.2, 0.2, 0.2]},
+                     "combine": {"total_ms": 0.0, "launches": 0, "ms": []}}}
+    t = bench.kernel_table(kt, {"dispatch": 1_000_000, "combine": 5}, cold=cold)
+    assert set(t) == {"dispatch"}                       # kernels with no launch are left out
+    assert t["dispatch"]["us"] == 100.0 and t["dispatch"]["GB/s"] == 10.0
+    assert t["dispatch"]["us_p10_p50_p90"] == [100.0, 100.0, 100.0]
+    assert t["dispatch"]["us_cold_p10_p50_p90"] == [200.0, 200.0, 200.0]
