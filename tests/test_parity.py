@@ -544,6 +544,69 @@ def test_launch_log(gpu, capfd, monkeypatch):
         assert "[moe_ep]" in err and name in err, err[-2000:]
 
 
+def test_contexts_on_concurrent_streams(gpu):
+    """Three contexts (bf16 send + contiguous, fp8 send + contiguous, fp8 low
+    latency) with their layout, dispatch and combine interleaved on three
+    streams and no synchronisation in between: the contexts share no state, so
+    each matches the oracle as if it had run alone."""
+    cases = []
+    for name, T in (("prefill", 700), ("grouped", 500), ("decode", 128)):
+        d = W.make(name, T=T)
+        c = d["cfg"]
+        ll = c["layout"] == W.LAYOUT_PADDED_LL
+        ctx = make_ctx(gpu, c, T)
+        M = ctx.cfg.max_tokens
+        ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"],
+                              max_tokens=M if ll else 0, with_send=not ll)
+        pos_ref = ref["pos_ll"] if ll else ref["pos"]
+        valid = ref["pos"] >= 0
+        yv = W.expert_outputs({"cfg": c}, ref["n_pairs"])
+        y = torch.empty((ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"]), c["H"]), dtype=torch.bfloat16,
+                        device=dev())
+        y.view(torch.int16).fill_(0x7FC0)
+        y[torch.from_numpy(pos_ref[valid].astype(np.int64)).to(dev())] = to_dev_bf16(yv[ref["pos"][valid]])
+        cases.append(dict(name=name, c=c, ll=ll, ctx=ctx, ref=ref, pos_ref=pos_ref, yv=yv, y=y,
+                          x=to_dev_bf16(d["x"]), idx=torch.from_numpy(d["topk_idx"]).to(dev()),
+                          w=torch.from_numpy(d["topk_weights"]).to(dev()), w_np=d["topk_weights"],
+                          bufs=gpu.DispatchBuffers(ctx), h=gpu.Handle(ctx), s=torch.cuda.Stream()))
+    for cs in cases:
+        cs["s"].wait_stream(torch.cuda.current_stream())   # inputs were copied on the default stream
+    log("concurrent contexts: %s" % ", ".join(cs["name"] for cs in cases))
+    # interleaved issue: layouts, then dispatches, then combines, each on its own stream
+    for cs in cases:
+        if not cs["ll"]:
+            with torch.cuda.stream(cs["s"]):
+                cs["layout"] = gpu.moe_dispatch_layout(cs["ctx"], cs["idx"])
+    for cs in reversed(cases):
+        with torch.cuda.stream(cs["s"]):
+            gpu.moe_dispatch(cs["ctx"], cs["x"], cs["idx"], reuse_layout=not cs["ll"], bufs=cs["bufs"],
+                             handle=cs["h"])
+    for cs in cases:
+        with torch.cuda.stream(cs["s"]):
+            cs["out"] = gpu.moe_combine(cs["ctx"], cs["y"], cs["w"], cs["h"])
+    torch.cuda.synchronize()
+    for cs in cases:
+        ref, c = cs["ref"], cs["c"]
+        st, flags = gpu.moe_poll_error(cs["ctx"])
+        assert st == gpu.MOE_OK, (cs["name"], st, flags)
+        if not cs["ll"]:
+            cnt_e, cnt_r, in_rank = cs["layout"]
+            assert np.array_equal(bits_of(cnt_e), ref["num_tokens_per_expert"]), cs["name"]
+            assert np.array_equal(bits_of(in_rank), ref["is_token_in_rank"]), cs["name"]
+            assert np.array_equal(bits_of(cs["bufs"].send_rows[:ref["n_send"]]).view(ref["send_rows"].dtype),
+                                  ref["send_rows"]), cs["name"]
+        T = c["T"]
+        assert np.array_equal(bits_of(cs["h"].pos[:T]), cs["pos_ref"]), cs["name"]
+        valid = ref["pos"] >= 0
+        dst = torch.from_numpy(cs["pos_ref"][valid].astype(np.int64)).to(dev())
+        got = bits_of(cs["bufs"].recv_rows[dst]).view(ref["recv_rows"].dtype)
+        assert np.array_equal(got, ref["recv_rows"][ref["pos"][valid]]), cs["name"]
+        assert np.array_equal(bits_of(cs["out"]), oracle.combine(cs["yv"], cs["w_np"], ref["pos"])), cs["name"]
+        cs["ctx"].close()
+    del cases
+    torch.cuda.empty_cache()
+
+
 def test_prepared_calls_match(gpu):
     """prepare_dispatch / prepare_combine give the same bytes as the plain calls."""
     d = W.make("decode")
