@@ -265,6 +265,21 @@ def test_limits(gpu):
     run_case(gpu, c, x, idx, w, max_tokens=c["T"], tag="limits")
 
 
+@pytest.mark.parametrize("quant,layout,T,k", [(W.QUANT_BF16, W.LAYOUT_CONTIGUOUS, 300, 8),
+                                              (W.QUANT_FP8, W.LAYOUT_CONTIGUOUS, 300, 8),
+                                              (W.QUANT_FP8, W.LAYOUT_PADDED_LL, 600, 4)])
+def test_max_hidden(gpu, quant, layout, T, k):
+    """The largest supported hidden size (32768: 4096 16-byte chunks per bf16
+    row) on the send + contiguous path and on the two-launch low-latency path
+    (T above the fused launch's limit)."""
+    c = dict(index=11, T=T, H=32768, E=16, R=4, k=k, quant=quant, layout=layout, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(32768 + quant + 2 * layout))
+    idx = W.route_uniform(rng, T, c["E"], k)
+    x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, T, k)
+    run_case(gpu, c, x, idx, w, reuse=(layout == W.LAYOUT_CONTIGUOUS), max_tokens=T, tag="max-hidden")
+
+
 # ---------------------------------------------------------------- fp8 codec
 def test_fp8_codec_exhaustive_bf16(gpu):
     """Blocks whose max is 448 quantise with scale exactly 1, so the GPU's
