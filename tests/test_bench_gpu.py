@@ -1,0 +1,57 @@
+"""bench.py's JSON line (GPU): a short run of the main step, of the decode step
+and of the backward step through the command line, checked for the fields the
+line must carry."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+QUICK = ["--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--no-decode", "--no-backward",
+         "--no-overlap", "--no-configs"]
+
+
+def run_bench(*args):
+    print("bench.py", " ".join(args), flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, lines                     # exactly one JSON line
+    return json.loads(lines[0])
+
+
+def check_line(d, steps, warmup):
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["value"] > 0 and d["ms_per_step"] > 0
+    assert "workload" in d["config"]
+    rf = d["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in rf, key
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    for k in d["kernels"].values():
+        assert k["us"] > 0 and len(k["us_p10_p50_p90"]) == 3
+
+
+def test_bench_line_prefill():
+    check_line(run_bench(*QUICK), 5, 2)
+
+
+def test_bench_line_decode():
+    d = run_bench("--workload", "decode", *QUICK)
+    check_line(d, 5, 2)
+    assert d["config"]["workload"].startswith("decode")
+
+
+def test_bench_line_backward_step():
+    d = run_bench("--step", "backward", *QUICK)
+    check_line(d, 5, 2)
+    assert set(d["kernels"]) == {"dispatch_bwd", "combine_bwd"}
