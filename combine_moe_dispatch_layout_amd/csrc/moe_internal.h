@@ -54,6 +54,7 @@ struct PackArgs {
     int32_t T, k, E, R, El, H;
     int32_t rbits;
     int32_t nslices;           // work items per token (row split)
+    int32_t ll_bpt;            // fused low-latency dispatch: blocks per token
     int32_t max_tokens;
     int32_t s0;
     int64_t cap;               // low-latency slots per expert (M * R)

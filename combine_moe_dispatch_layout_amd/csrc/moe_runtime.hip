@@ -481,21 +481,21 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     int chunks, nslices;
     row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, 1, &chunks, &nslices);
     a.nslices = nslices;
+    a.ll_bpt = 1;
     // at least one block so that the handle's offsets and counts are written for T = 0
     PackArgs a0 = a;
     if (num_tokens == 0) a0.T = 0;
     TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH);
     hipError_t e;
     if (fused) {
-        // one block per token whose wavefronts split the row into slices: 1024
-        // threads when the row has more than 256 chunks (the context's layout
-        // state is neither read nor written here)
+        // ll_bpt blocks per token whose wavefronts each copy one 64-chunk slice:
+        // 512-thread blocks when the row has more than 256 chunks (the
+        // context's layout state is neither read nor written here)
         const int64_t nchunk = c.hidden / 8;
-        const int nt = nchunk > kBlockThreads ? 1024 : kBlockThreads;
-        int cf = 1;
-        while (cf < 16 && (int64_t)nt * cf < nchunk) cf *= 2;
-        a.nslices = (int)((nchunk + 64 * cf - 1) / (64 * cf));
-        e = launch_ll_fused(a, cf, nt, fp8, s);
+        const int nt = nchunk > kBlockThreads ? 512 : kBlockThreads;
+        a.nslices = (int)((nchunk + 63) / 64);
+        a.ll_bpt = (a.nslices + nt / 64 - 1) / (nt / 64);
+        e = launch_ll_fused(a, 1, nt, fp8, s);
     } else if (num_tokens == 0) {
         // grid of one block: block 0 copies the offsets, every wave exits (no items)
         a0.nslices = 1;
