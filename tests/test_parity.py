@@ -414,14 +414,16 @@ def test_expert_rank_extremes(gpu, E, R, k):
 
 # ---------------------------------------------------------------- resource control and hooks
 @pytest.mark.parametrize("max_wg", [1, 3, 64, 1000])
-@pytest.mark.parametrize("name", ["prefill", "grouped"])
-def test_max_workgroups_same_results(gpu, name, max_wg):
-    """A capped grid (each workgroup loops over more rows) gives the same bytes."""
+@pytest.mark.parametrize("name,T", [("prefill", 700), ("grouped", 700), ("decode", 700), ("decode", 128)])
+def test_max_workgroups_same_results(gpu, name, T, max_wg):
+    """A capped grid (each workgroup loops over more rows) gives the same bytes.
+    Low latency at 700 tokens runs layout + pack (capped); at 128 tokens the
+    fused dispatch, which the cap does not apply to."""
     c = small_cfg(name, H=1024)
-    d = W.make(name, T=700)
-    c["max_tokens"] = 700
-    run_case(gpu, c, d["x"][:, :c["H"]].copy(), d["topk_idx"], d["topk_weights"], max_tokens=700,
-             tag="maxwg-%s" % name, max_workgroups=max_wg)
+    d = W.make(name, T=T)
+    c["max_tokens"] = T
+    run_case(gpu, c, d["x"][:, :c["H"]].copy(), d["topk_idx"], d["topk_weights"], max_tokens=T,
+             reuse=(name != "decode"), tag="maxwg-%s-%d" % (name, T), max_workgroups=max_wg)
 
 
 def test_max_workgroups_full_prefill(gpu):
