@@ -112,10 +112,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // are cut into more slices when there are too few tokens to keep ~8
 // wavefronts per CU in flight.  Measured on MI355X: with its non-temporal
 // row stores the dispatch is fastest with one chunk per lane (5-11% ahead of
-// whole rows per wavefront on the prefill, grouped and skewed shapes); so is
-// the combine, which loads all of a slice's rows at once (1-2% ahead of two
-// chunks per lane); the combine backward wants at most 8 slices per token
-// (one chunk per lane up to 512 chunks per row, then two).
+// whole rows per wavefront on the prefill, grouped and skewed shapes).  The
+// combine (and the dispatch backward, the same kernel) takes two: one chunk
+// per lane is 1-2% faster with warm caches but 12-15% slower when the caches
+// hold other kernels' dirty lines.  The combine backward wants at most 8
+// slices per token (one chunk per lane up to 512 chunks per row, then two),
+// which is faster in every cache state measured.
 void row_split(int64_t T, int64_t nchunk, int forced, int cap, int* chunks, int* nslices) {
     int c;
     if (forced > 0) {
@@ -534,7 +536,7 @@ MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float
     a.rows_cap = ctx->g.recv_rows;
     a.err = ctx->err();
     int chunks, nslices;
-    row_split(T, c.hidden / 8, ctx->combine_chunks, 1, &chunks, &nslices);
+    row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_COMBINE);
@@ -566,7 +568,7 @@ MOE_API moe_status moe_dispatch_backward(moe_ctx* ctx, const void* grad_recv, co
     a.rows_cap = ctx->g.recv_rows;
     a.err = ctx->err();
     int chunks, nslices;
-    row_split(T, c.hidden / 8, ctx->combine_chunks, 1, &chunks, &nslices);
+    row_split(T, c.hidden / 8, ctx->combine_chunks, 2, &chunks, &nslices);
     a.nslices = nslices;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH_BWD);
