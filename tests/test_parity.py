@@ -56,7 +56,7 @@ def poison(bufs):
 
 
 def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, check_poison=True,
-             tag="", max_workgroups=0, side_stream=False):
+             tag="", max_workgroups=0, side_stream=False, tune=None):
     """Layout + dispatch + combine on the GPU and in the oracle; compare all."""
     T = idx.shape[0]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
@@ -67,6 +67,8 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
     if max_workgroups:
         ctx.set_max_workgroups(max_workgroups)
+    if tune is not None:
+        ctx.tune(*tune)                          # (dispatch, combine) chunks per lane
     M = ctx.cfg.max_tokens
     ref = oracle.dispatch(x_bits, idx, c["E"], c["R"], quant=c["quant"],
                           max_tokens=M if ll else 0, src_rank=src_rank, with_send=not ll)
@@ -410,6 +412,22 @@ def test_expert_rank_extremes(gpu, E, R, k):
     x = W.to_bf16_bits(rng.standard_normal((T, 128), dtype=np.float32))
     w = W.softmax_weights(rng, T, k)
     run_case(gpu, c, x, idx, w, max_tokens=T, tag="extremes")
+
+
+# ---------------------------------------------------------------- launch-geometry overrides
+@pytest.mark.parametrize("chunks", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("name,H", [("prefill", 7168), ("prefill", 2176), ("grouped", 7168), ("decode", 2176)])
+def test_row_split_overrides(gpu, name, H, chunks):
+    """Every chunks-per-lane setting of moe_ctx_tune for the dispatch and the
+    combine (1-16; the defaults use 1 and 2) gives the oracle's bytes, on full
+    and ragged rows; the low-latency case runs layout + pack (T above the
+    fused launch's limit)."""
+    c = small_cfg(name, H=H)
+    T = 600
+    d = W.make(name, T=T)
+    c["max_tokens"] = T
+    run_case(gpu, c, np.ascontiguousarray(d["x"][:, :H]), d["topk_idx"], d["topk_weights"], max_tokens=T,
+             reuse=(name != "decode"), tag="tune-%s-%d-%d" % (name, H, chunks), tune=(chunks, chunks))
 
 
 # ---------------------------------------------------------------- resource control and hooks
