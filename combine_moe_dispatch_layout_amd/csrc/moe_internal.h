@@ -11,6 +11,9 @@ namespace moe {
 constexpr int kTileTokens = 256;
 constexpr int kBlockThreads = 256;
 constexpr int kWavesPerBlock = kBlockThreads / 64;
+// The combine (and the dispatch backward, the same kernel) runs one wavefront
+// per workgroup: measured on MI355X, ~2% faster than four, warm or cold.
+constexpr int kCombineThreads = 64;
 
 // The fused low-latency dispatch handles up to this many (token, slot) entries
 // and tokens.

@@ -811,12 +811,13 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
 }
 
 template <int C, int KMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_combine(CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
+    constexpr int kWaves = kCombineThreads / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int64_t total = (int64_t)a.T * a.nslices;
-    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + w; item < total; item += stride)
+    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    for (int64_t item = (int64_t)blockIdx.x * kWaves + w; item < total; item += stride)
         combine_item<C, KMAX>(a, item, lane);
 }
 
@@ -982,9 +983,9 @@ hipError_t pack_c(const PackArgs& a, bool fp8, bool ll, bool send, dim3 grid, hi
 
 template <int C>
 hipError_t combine_c(const CombineArgs& a, int kmax, dim3 grid, hipStream_t st) {
-    if (kmax <= 8) hipLaunchKernelGGL((k_combine<C, 8>), grid, dim3(kBlockThreads), 0, st, a);
-    else if (kmax <= 16) hipLaunchKernelGGL((k_combine<C, 16>), grid, dim3(kBlockThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_combine<C, 32>), grid, dim3(kBlockThreads), 0, st, a);
+    if (kmax <= 8) hipLaunchKernelGGL((k_combine<C, 8>), grid, dim3(kCombineThreads), 0, st, a);
+    else if (kmax <= 16) hipLaunchKernelGGL((k_combine<C, 16>), grid, dim3(kCombineThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<C, 32>), grid, dim3(kCombineThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1001,8 +1002,8 @@ hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, int max_b
 // At least one block: block 0 of the dispatch kernel also writes the handle's
 // offsets and counts, which must happen even when there are no tokens.
 // max_blocks > 0 caps the grid (the kernels loop over their items).
-dim3 items_grid(int64_t items, int max_blocks) {
-    int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+dim3 items_grid(int64_t items, int max_blocks, int waves_per_block = kWavesPerBlock) {
+    int64_t blocks = (items + waves_per_block - 1) / waves_per_block;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
     return dim3((unsigned)(blocks > 0 ? blocks : 1));
 }
@@ -1052,7 +1053,7 @@ hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8,
 }
 
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {
-    const dim3 grid = items_grid((int64_t)a.T * a.nslices, max_blocks);
+    const dim3 grid = items_grid((int64_t)a.T * a.nslices, max_blocks, kCombineThreads / 64);
     switch (chunks) {
         case 1: return combine_c<1>(a, kmax, grid, s);
         case 2: return combine_c<2>(a, kmax, grid, s);
