@@ -1002,7 +1002,7 @@ hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, int max_b
 // At least one block: block 0 of the dispatch kernel also writes the handle's
 // offsets and counts, which must happen even when there are no tokens.
 // max_blocks > 0 caps the grid (the kernels loop over their items).
-dim3 items_grid(int64_t items, int max_blocks, int waves_per_block = kWavesPerBlock) {
+dim3 items_grid(int64_t items, int64_t max_blocks, int waves_per_block = kWavesPerBlock) {
     int64_t blocks = (items + waves_per_block - 1) / waves_per_block;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
     return dim3((unsigned)(blocks > 0 ? blocks : 1));
@@ -1053,7 +1053,9 @@ hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8,
 }
 
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {
-    const dim3 grid = items_grid((int64_t)a.T * a.nslices, max_blocks, kCombineThreads / 64);
+    // a cap counts 256-thread workgroups: the same wavefronts as one-wavefront workgroups
+    const int64_t cap = max_blocks > 0 ? (int64_t)max_blocks * (kBlockThreads / kCombineThreads) : 0;
+    const dim3 grid = items_grid((int64_t)a.T * a.nslices, cap, kCombineThreads / 64);
     switch (chunks) {
         case 1: return combine_c<1>(a, kmax, grid, s);
         case 2: return combine_c<2>(a, kmax, grid, s);

@@ -289,12 +289,14 @@ moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float*
  * `max_workgroups` workgroups (0 = no cap, the default) run the dispatch
  * (layout-reusing or two-launch path), combine and backward kernels of this
  * context; each workgroup then loops over more rows, so results are
- * unchanged.  A workgroup is 256 threads for the dispatch, one wavefront (64
- * threads) for the combine and the dispatch backward, and 64 threads per row
- * slice (up to 1024) for the combine backward.  The layout kernel (a few
- * workgroups) and the fused low-latency dispatch (the pages: low-latency
- * kernels need no SM control) are not capped.  Capping leaves compute units to kernels on other streams,
- * e.g. GEMMs overlapped with dispatch and combine. */
+ * unchanged.  A workgroup is 256 threads for the dispatch and 64 threads per
+ * row slice (up to 1024) for the combine backward; the combine and the
+ * dispatch backward run one-wavefront workgroups, 4 * max_workgroups of them
+ * (the wavefronts of max_workgroups 256-thread workgroups).  The layout
+ * kernel (a few workgroups) and the fused low-latency dispatch (the pages:
+ * low-latency kernels need no SM control) are not capped.  Capping leaves
+ * compute units to kernels on other streams, e.g. GEMMs overlapped with
+ * dispatch and combine. */
 moe_status moe_ctx_set_max_workgroups(moe_ctx* ctx, int32_t max_workgroups);
 
 /* Issue/complete split (the guide's hook-based communication-computation
