@@ -371,3 +371,60 @@ def test_backward_api_errors(gpu):
     torch.cuda.synchronize()
     ctx.close()
     other.close()
+
+
+@pytest.mark.parametrize("name,T", [("prefill", 700), ("decode", 128)])
+def test_backward_graph_capture(gpu, name, T):
+    """The backward calls only enqueue kernels, so a backward step captures into
+    a HIP graph: replay it several times, with eager work and a synchronisation
+    between replays, and compare every replay with the eager step."""
+    c = small_cfg(name)
+    d = W.make(name, T=T)
+    c["max_tokens"] = T
+    ctx = gpu.Context(gpu.make_config(T, c["H"], c["E"], c["R"], c["k"], 0, c["quant"], c["layout"]))
+    x = to_dev_bf16(np.ascontiguousarray(d["x"][:, :c["H"]]))
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    bufs, h = gpu.DispatchBuffers(ctx), gpu.Handle(ctx)
+    gpu.moe_dispatch(ctx, x, idx, bufs=bufs, handle=h)
+    n_cap = ctx.hint(gpu.MOE_BUF_EXPERT_OUT) // (2 * c["H"])
+    g = torch.Generator(device=dev())
+    g.manual_seed(11)
+    grad_recv = torch.randn((n_cap, c["H"]), generator=g, device=dev()).to(torch.bfloat16)
+    y = torch.randn((n_cap, c["H"]), generator=g, device=dev()).to(torch.bfloat16)
+    grad_out = torch.randn((T, c["H"]), generator=g, device=dev()).to(torch.bfloat16)
+    grad_x = torch.empty((T, c["H"]), dtype=torch.bfloat16, device=dev())
+    grad_y = torch.empty_like(y)
+    grad_w = torch.empty((T, c["k"]), dtype=torch.float32, device=dev())
+
+    def step():
+        gpu.moe_dispatch_backward(ctx, grad_recv, h, grad_x=grad_x)
+        gpu.moe_combine_backward(ctx, grad_out, w, y, h, grad_expert_out=grad_y, grad_weights=grad_w)
+
+    watch = [grad_x, grad_y, grad_w]
+    for t in watch:
+        t.view(torch.uint8).fill_(0x5A)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in watch]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        log("backward graph replay %d (%s)" % (rep, name))
+        for t in watch:                       # eager work between replays
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(watch, eager)):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), ("replay", rep, "tensor", i)
+    st, _ = gpu.moe_poll_error(ctx)
+    assert st == gpu.MOE_OK
+    del graph
+    ctx.close()
