@@ -1039,15 +1039,8 @@ hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8,
         else hipLaunchKernelGGL((k_ll_dispatch<CC, false, NT>), grid, dim3(NT), 0, s, a);             \
         return hipGetLastError();                                                                     \
     }
-    MOE_LL_CASE(1, 256)
-    MOE_LL_CASE(2, 256)
-    MOE_LL_CASE(4, 256)
-    MOE_LL_CASE(8, 256)
-    MOE_LL_CASE(16, 256)
-    MOE_LL_CASE(1, 512)
-    MOE_LL_CASE(1, 1024)
-    MOE_LL_CASE(2, 1024)
-    MOE_LL_CASE(4, 1024)
+    MOE_LL_CASE(1, 256)   // rows of up to 256 chunks
+    MOE_LL_CASE(1, 512)   // longer rows, ll_bpt blocks per token
 #undef MOE_LL_CASE
     return hipErrorInvalidValue;
 }
