@@ -131,10 +131,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+# torch's raw current-stream query: ~0.1 us against ~2.7 us for building a
+# torch.cuda.Stream object per call (half of an eager decode step's host time
+# otherwise); the public API is the fallback where the query is missing
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream=None):
     """HIP stream handle of a torch stream (default: the current stream)."""
-    st = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(st.cuda_stream)
+    if stream is None:
+        if _raw_current_stream is not None:
+            return ctypes.c_void_p(_raw_current_stream(torch.cuda.current_device()))
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def make_config(max_tokens, hidden, num_experts, num_ranks, topk, src_rank=0,

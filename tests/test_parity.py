@@ -642,6 +642,20 @@ def test_contexts_on_concurrent_streams(gpu):
     torch.cuda.empty_cache()
 
 
+def test_current_stream_handle(gpu):
+    """The binding's current-stream handle is torch's, on the default stream
+    and inside a side-stream context."""
+    from combine_moe_dispatch_layout_amd import _binding as B
+
+    def handle(s):                       # c_void_p(0).value is None: the null stream
+        return s.value or 0
+    assert handle(B._stream()) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert handle(B._stream()) == side.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert handle(B._stream(side)) == side.cuda_stream
+
+
 def test_prepared_calls_match(gpu):
     """prepare_dispatch / prepare_combine give the same bytes as the plain calls."""
     d = W.make("decode")
