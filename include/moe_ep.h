@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 2
+#define MOE_EP_ABI_VERSION 3   /* 3: moe_timing_launches */
 
 /* ---------------------------------------------------------------- status */
 typedef enum moe_status {
@@ -152,9 +152,11 @@ moe_status moe_ctx_config(const moe_ctx* ctx, moe_config* out);
 
 /* Launch-geometry override, for measurement sweeps: 16-byte chunks each lane
  * moves per work item in the dispatch and combine kernels (1, 2, 4, 8 or 16;
- * 0 = the built-in choice, which keeps whole rows per wavefront when there
- * are enough tokens to fill the chip and splits rows otherwise).  Results do
- * not depend on it. */
+ * the combine value also applies to both backward kernels).  0 = the built-in
+ * choice: one chunk per lane for the dispatch, two for the combine and the
+ * dispatch backward, at most 8 row slices per token for the combine backward,
+ * fewer chunks per lane when there are too few tokens to fill the chip.  The
+ * fused low-latency dispatch ignores it.  Results do not depend on it. */
 moe_status moe_ctx_tune(moe_ctx* ctx, int32_t dispatch_chunks, int32_t combine_chunks);
 
 /* ---------------------------------------------------------------- layout */
