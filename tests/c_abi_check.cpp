@@ -8,6 +8,13 @@
 //  * with the expert outputs equal to the received rows (an identity expert)
 //    and weights that sum to exactly one (powers of two), combine returns x
 //    bit for bit.
+//  * backward, with the gradient rows equal to the received rows: dispatch
+//    backward returns bf16(n_valid(t) * x[t]); combine backward with the output
+//    gradient x and the identity expert outputs gives grad_w[t, j] = sum_h
+//    x[t, h]^2 (exact in fp32 for these small integers) and grad_y rows
+//    w * x[t] (exact: powers of two);
+//  * a hook recorded after the backward and waited on another stream, and the
+//    per-launch timing calls.
 // Prints one line and exits 0 on success, 1 on a mismatch, 2 on an API error.
 #include <hip/hip_runtime.h>
 
@@ -40,6 +47,19 @@ static uint16_t bf16_of_small_int(int v) {   // exact for |v| < 256
     uint32_t u;
     std::memcpy(&u, &f, 4);
     return (uint16_t)(u >> 16);
+}
+
+static float f32_of_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint16_t bf16_rne(float f) {   // round to nearest even (finite values)
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
 int main() {
@@ -132,11 +152,72 @@ int main() {
         const uint16_t want = hx[i] == 0x8000 ? 0 : hx[i];   // -0 comes back as +0
         if (hout[i] != want) bad |= 8;
     }
+    // ---- backward (timed, completed on a second stream through a hook)
+    void *gx, *gy;
+    float* gw;
+    HIPCHK(hipMalloc(&gx, hout.size() * 2));
+    HIPCHK(hipMalloc(&gy, hint(MOE_BUF_EXPERT_OUT)));
+    HIPCHK(hipMalloc(&gw, hw.size() * 4));
+    API(moe_timing_begin(ctx, 4));
+    API(moe_dispatch_backward(ctx, recv, &h, gx, s));          // gradient rows = the received rows
+    API(moe_combine_backward(ctx, x, w, recv, &h, gy, gw, s));  // output gradient = x, identity experts
+    moe_hook* hook = nullptr;
+    API(moe_hook_create(&hook));
+    API(moe_hook_record(hook, s));
+    hipStream_t s2;
+    HIPCHK(hipStreamCreate(&s2));
+    API(moe_hook_wait(hook, s2));
+    HIPCHK(hipStreamSynchronize(s2));
+    int32_t kids[4] = {-1, -1, -1, -1}, nl = 0;
+    float ms[4] = {};
+    API(moe_timing_launches(ctx, kids, ms, 4, &nl));
+    double tot[MOE_KERNEL_COUNT];
+    int64_t cnt[MOE_KERNEL_COUNT];
+    API(moe_timing_end(ctx, tot, cnt));
+    if (nl != 2 || kids[0] != MOE_KERNEL_DISPATCH_BWD || kids[1] != MOE_KERNEL_COMBINE_BWD || !(ms[0] > 0.f) ||
+        cnt[MOE_KERNEL_COMBINE_BWD] != 1)
+        bad |= 16;
+    API(moe_poll_error(ctx, s, &flags));
+    std::vector<uint16_t> hgx(hout.size()), hgy((size_t)valid * H);
+    std::vector<float> hgw(hw.size());
+    HIPCHK(hipMemcpy(hgx.data(), gx, hgx.size() * 2, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(hgw.data(), gw, hgw.size() * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(hgy.data(), gy, hgy.size() * 2, hipMemcpyDeviceToHost));
+    std::vector<int32_t> hpos((size_t)T * k);
+    HIPCHK(hipMemcpy(hpos.data(), h.pos, hpos.size() * 4, hipMemcpyDeviceToHost));
+    for (int t = 0; t < T; ++t) {
+        int nv = 0;
+        double sq = 0.0;
+        for (int j = 0; j < k; ++j) nv += hidx[(size_t)t * k + j] >= 0;
+        for (int hh = 0; hh < H; ++hh) {
+            const float v = f32_of_bf16(hx[(size_t)t * H + hh]);
+            sq += (double)v * v;
+            const uint16_t want = bf16_rne((float)nv * v);
+            const uint16_t got = hgx[(size_t)t * H + hh];
+            if (got != want && !(got == 0 && want == 0x8000)) bad |= 32;   // -0 sums to +0
+        }
+        for (int j = 0; j < k; ++j) {
+            const int p = hpos[(size_t)t * k + j];
+            const float gwv = hgw[(size_t)t * k + j];
+            if (p < 0) {
+                if (gwv != 0.f) bad |= 64;
+                continue;
+            }
+            if ((double)gwv != sq) bad |= 64;
+            const float wt = hw[(size_t)t * k + j];
+            for (int hh = 0; hh < H; ++hh) {
+                const uint16_t want = bf16_rne(wt * f32_of_bf16(hx[(size_t)t * H + hh]));
+                if (hgy[(size_t)p * H + hh] != want) bad |= 128;
+            }
+        }
+    }
     std::printf("c_abi_check: T=%d H=%d E=%d R=%d k=%d valid slots %ld, flags %u, result %s (%d)\n", T, H, E, R, k,
                 valid, flags, bad ? "MISMATCH" : "ok", bad);
 
+    API(moe_hook_destroy(hook));
+    HIPCHK(hipStreamDestroy(s2));
     void* bufs_to_free[] = {x, idx, w, send, recv, out, cnt_e, cnt_r, in_rank, h.pos, h.expert_offsets,
-                            h.rank_offsets, h.send_src_idx, h.recv_src_idx, h.recv_counts};
+                            h.rank_offsets, h.send_src_idx, h.recv_src_idx, h.recv_counts, gx, gy, gw};
     for (void* p : bufs_to_free) HIPCHK(hipFree(p));
     HIPCHK(hipStreamDestroy(s));
     API(moe_ctx_destroy(ctx));

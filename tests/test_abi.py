@@ -147,8 +147,10 @@ def test_product_does_not_reference_oracle():
 @pytest.mark.gpu
 def test_c_consumer_runs():
     """tests/c_abi_check (built by __graft_entry__.build()) drives layout,
-    dispatch and combine through the C ABI with no Python in between and checks
-    closed-form properties (counts, receive rows, identity round trip)."""
+    dispatch, combine, both backward calls, a hook and the per-launch timing
+    through the C ABI with no Python in between and checks closed-form
+    properties (counts, receive rows, identity round trip, gradients of
+    small-integer inputs)."""
     exe = os.path.join(ROOT, "tests", "c_abi_check")
     if not os.path.exists(exe):
         pytest.fail("tests/c_abi_check is not built (run __graft_entry__.build())")
