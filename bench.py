@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--step", default="forward", choices=["forward", "backward"],
                    help="which step the main line times: forward (layout + dispatch + combine) or "
                         "backward (dispatch backward + combine backward)")
-    p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="host CPU time the oracle baseline runs for (whole steps, at least 3)")
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + steps only (for rocprofv3), print the JSON line without baselines")
     p.add_argument("--copy-calibration", action="store_true",
@@ -395,8 +396,10 @@ def host_cpu():
     return model, len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(s, reps):
-    """The oracle as it stands (single-threaded scalar C) on the same inputs."""
+def cpu_baseline(s, seconds, min_reps=3, max_reps=100000):
+    """The oracle as it stands (single-threaded scalar C) on the same inputs:
+    whole steps, repeated until about `seconds` of CPU time (at least
+    min_reps).  Returns (median seconds per step, steps run, total seconds)."""
     import numpy as np
     import oracle
     d, c = s["d"], s["c"]
@@ -405,13 +408,13 @@ def cpu_baseline(s, reps):
     os.sched_setaffinity(0, {min(saved)})
     y = s["y"][:s["n_pairs"]].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
     times = []
-    for _ in range(reps):
+    while len(times) < min_reps or (sum(times) < seconds and len(times) < max_reps):
         t0 = time.perf_counter()
         r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
         oracle.combine(y, d["topk_weights"], r["pos"])
         times.append(time.perf_counter() - t0)
     os.sched_setaffinity(0, saved)
-    return float(np.median(times)), r
+    return float(np.median(times)), len(times), float(sum(times))
 
 
 def main():
@@ -565,13 +568,13 @@ def main():
 
     if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
         model, ncpu = host_cpu()
-        sec, _ = cpu_baseline(s, a.cpu_reps)
+        sec, runs, total = cpu_baseline(s, a.cpu_seconds)
         line["cpu_baseline"] = {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle",
                                 "sample": "the full %s workload (%d tokens): layout, positions, payload "
-                                          "rows and combine in the scalar C oracle, median of %d runs, "
-                                          "%.2f s each, pinned to one of %d host cores (%s)" % (
-                                              a.workload, T, a.cpu_reps, sec, ncpu, model)}
+                                          "rows and combine in the scalar C oracle, median of %d runs "
+                                          "(%.2f s each, %.1f s in all), pinned to one of %d host cores "
+                                          "(%s)" % (a.workload, T, runs, sec, total, ncpu, model)}
     print(json.dumps(line), flush=True)
     s["ctx"].close()
 

@@ -80,3 +80,19 @@ def test_kernel_table_reports_percentiles_and_cold_passes():
     assert t["dispatch"]["us"] == 100.0 and t["dispatch"]["GB/s"] == 10.0
     assert t["dispatch"]["us_p10_p50_p90"] == [100.0, 100.0, 100.0]
     assert t["dispatch"]["us_cold_p10_p50_p90"] == [200.0, 200.0, 200.0]
+
+
+def test_cpu_baseline_runs_whole_steps_for_the_time_asked():
+    """The oracle baseline repeats whole steps until the CPU time asked for is
+    spent (at least three), and reports the median step."""
+    import torch
+    d = W.make("tiny")
+    c = d["cfg"]
+    ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
+    n = ref["n_pairs"]
+    y = torch.from_numpy(W.expert_outputs(d, n).view(np.int16)).view(torch.bfloat16)
+    s = {"d": d, "c": c, "y": y, "n_pairs": n}
+    med, runs, total = bench.cpu_baseline(s, 0.0)
+    assert runs == 3 and med > 0 and total >= med
+    med, runs, total = bench.cpu_baseline(s, 0.2)
+    assert total >= 0.2 and runs > 3 and med <= total
