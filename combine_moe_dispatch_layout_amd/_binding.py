@@ -168,6 +168,9 @@ class Context:
         _check(lib.moe_ctx_create(ctypes.byref(cfg), ctypes.byref(h)), "moe_ctx_create")
         self._h = h
         self.device = torch.cuda.current_device()
+        # identifies this context (and so its configuration) to the buffer
+        # checks of the calls; a fresh object per context
+        self._fit_token = object()
 
     @property
     def handle(self):
@@ -300,6 +303,54 @@ def _as_dev(t, dtype, name):
     return t
 
 
+def _out(t, dtype, numel, name):
+    """A caller-supplied output: contiguous, of the right dtype, at least numel elements."""
+    _as_dev(t, dtype, name)
+    if t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs %d" % (name, t.numel(), numel))
+    return t
+
+
+def _fits(ctx, obj, parts, what):
+    """The kernels write a handle's arrays and the dispatch buffers through raw
+    pointers, up to the sizes moe_size_hint gives for the context's
+    configuration: check that every part is at least that large (and that the
+    C struct still points at it), once per (object, context)."""
+    key = ctx._fit_token
+    if getattr(obj, "_fits_key", None) is key:
+        return
+    for t, kind, ptr in parts:
+        need = ctx.hint(kind)
+        if t is None:
+            if need:
+                raise ValueError("%s lacks a buffer this configuration needs (kind %d)" % (what, kind))
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < need:
+            raise ValueError("%s was not made for this context's configuration (kind %d: %d bytes, needs %d)"
+                             % (what, kind, t.numel() * t.element_size(), need))
+        if ptr != t.data_ptr():
+            raise ValueError("%s: the C struct no longer points at its tensors" % what)
+    obj._fits_key = key
+
+
+def _check_handle(ctx, h):
+    c = h.c
+    _fits(ctx, h, ((h.pos, MOE_BUF_HANDLE_POS, c.pos), (h.expert_offsets, MOE_BUF_HANDLE_EXPERT_OFFSETS,
+                                                       c.expert_offsets),
+                   (h.rank_offsets, MOE_BUF_HANDLE_RANK_OFFSETS, c.rank_offsets),
+                   (h.send_src_idx, MOE_BUF_HANDLE_SEND_SRC, c.send_src_idx),
+                   (h.recv_src_idx, MOE_BUF_HANDLE_RECV_SRC, c.recv_src_idx),
+                   (h.recv_counts, MOE_BUF_HANDLE_RECV_COUNTS, c.recv_counts)), "handle")
+
+
+def _check_bufs(ctx, b):
+    c = b.c
+    _fits(ctx, b, ((b.send_rows, MOE_BUF_SEND_ROWS, c.send_rows or 0),
+                   (b.send_scales, MOE_BUF_SEND_SCALES, c.send_scales or 0),
+                   (b.recv_rows, MOE_BUF_RECV_ROWS, c.recv_rows or 0),
+                   (b.recv_scales, MOE_BUF_RECV_SCALES, c.recv_scales or 0)), "dispatch buffers")
+
+
 def moe_dispatch_layout(ctx, topk_idx, num_tokens_per_expert=None, num_tokens_per_rank=None,
                         is_token_in_rank=None):
     """Returns (num_tokens_per_expert int32[E], num_tokens_per_rank int32[R],
@@ -316,6 +367,9 @@ def moe_dispatch_layout(ctx, topk_idx, num_tokens_per_expert=None, num_tokens_pe
         num_tokens_per_rank = torch.empty(c.num_ranks, dtype=torch.int32, device=dev)
     if is_token_in_rank is None:
         is_token_in_rank = torch.empty((T, c.num_ranks), dtype=torch.uint8, device=dev)
+    _out(num_tokens_per_expert, torch.int32, c.num_experts, "num_tokens_per_expert")
+    _out(num_tokens_per_rank, torch.int32, c.num_ranks, "num_tokens_per_rank")
+    _out(is_token_in_rank, torch.uint8, T * c.num_ranks, "is_token_in_rank")
     _check(load_library().moe_dispatch_layout(
         ctx.handle, _ptr(topk_idx), T, _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
         _ptr(is_token_in_rank), _stream()), "moe_dispatch_layout")
@@ -335,6 +389,8 @@ def moe_dispatch(ctx, x, topk_idx, reuse_layout=False, bufs=None, handle=None):
         bufs = DispatchBuffers(ctx)
     if handle is None:
         handle = Handle(ctx)
+    _check_bufs(ctx, bufs)
+    _check_handle(ctx, handle)
     _check(load_library().moe_dispatch(ctx.handle, _ptr(x), _ptr(topk_idx), T, int(bool(reuse_layout)),
                                        ctypes.byref(bufs.c), ctypes.byref(handle.c), _stream()),
            "moe_dispatch")
@@ -353,6 +409,7 @@ def moe_combine(ctx, expert_out, topk_weights, handle, out=None):
         raise ValueError("expert_out smaller than MOE_BUF_EXPERT_OUT")
     if out is None:
         out = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=expert_out.device)
+    _out(out, torch.bfloat16, T * c.hidden, "out")
     _check(load_library().moe_combine(ctx.handle, _ptr(expert_out), _ptr(topk_weights),
                                       ctypes.byref(handle.c), _ptr(out), _stream()), "moe_combine")
     return out
@@ -418,6 +475,8 @@ def prepare_dispatch(ctx, x, topk_idx, reuse_layout, bufs, handle, stream=None):
     T = x.shape[0]
     if x.dim() != 2 or x.shape[1] != c.hidden or tuple(topk_idx.shape) != (T, c.topk):
         raise ValueError("x must be [T, %d] and topk_idx [T, %d]" % (c.hidden, c.topk))
+    _check_bufs(ctx, bufs)
+    _check_handle(ctx, handle)
     f = load_library().moe_dispatch
     args = (ctx.handle, _ptr(x), _ptr(topk_idx), ctypes.c_int32(T), ctypes.c_int32(int(bool(reuse_layout))),
             ctypes.byref(bufs.c), ctypes.byref(handle.c), _stream(stream))

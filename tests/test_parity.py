@@ -370,6 +370,49 @@ def test_api_errors(gpu):
     ctx2.close()
 
 
+def test_binding_rejects_buffers_of_another_configuration(gpu):
+    """The binding checks caller-supplied buffers, handles and outputs against
+    the sizes the context's configuration needs before anything is launched
+    (the C ABI takes raw pointers and cannot)."""
+    c = small_cfg("prefill", H=256)
+    d = W.make("prefill", T=64)
+    small = make_ctx(gpu, c, 32, max_tokens=32)
+    big = make_ctx(gpu, c, 64, max_tokens=64)
+    x = to_dev_bf16(d["x"][:, :256].copy())
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    h_small, b_small = gpu.Handle(small), gpu.DispatchBuffers(small)
+    h_big, b_big = gpu.Handle(big), gpu.DispatchBuffers(big)
+    with pytest.raises(ValueError, match="handle"):
+        gpu.moe_dispatch(big, x, idx, bufs=b_big, handle=h_small)
+    with pytest.raises(ValueError, match="dispatch buffers"):
+        gpu.moe_dispatch(big, x, idx, bufs=b_small, handle=h_big)
+    with pytest.raises(ValueError, match="handle"):
+        gpu.prepare_dispatch(big, x, idx, False, b_big, h_small)
+    # a struct that no longer points at its tensors
+    h_swapped = gpu.Handle(big)
+    h_swapped.pos = torch.empty_like(h_swapped.pos)
+    with pytest.raises(ValueError, match="no longer points"):
+        gpu.moe_dispatch(big, x, idx, bufs=b_big, handle=h_swapped)
+    # outputs too small or of the wrong type
+    with pytest.raises(ValueError, match="is_token_in_rank"):
+        gpu.moe_dispatch_layout(big, idx, is_token_in_rank=torch.empty((63, c["R"]), dtype=torch.uint8,
+                                                                        device=dev()))
+    with pytest.raises(TypeError, match="num_tokens_per_expert"):
+        gpu.moe_dispatch_layout(big, idx, num_tokens_per_expert=torch.empty(c["E"], dtype=torch.int64,
+                                                                             device=dev()))
+    gpu.moe_dispatch(big, x, idx, bufs=b_big, handle=h_big)
+    y = torch.zeros((big.hint(gpu.MOE_BUF_EXPERT_OUT) // 512, 256), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(ValueError, match="out"):
+        gpu.moe_combine(big, y, w, h_big, out=torch.empty((63, 256), dtype=torch.bfloat16, device=dev()))
+    # the same objects pass for a context of the same configuration, and the run is clean
+    out = gpu.moe_combine(big, y, w, h_big)
+    st, _ = gpu.moe_poll_error(big)
+    assert st == gpu.MOE_OK and tuple(out.shape) == (64, 256)
+    small.close()
+    big.close()
+
+
 def test_timing_api(gpu):
     d = W.make("tiny")
     c = d["cfg"]
