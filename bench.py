@@ -396,6 +396,20 @@ def host_cpu():
     return model, len(os.sched_getaffinity(0))
 
 
+def host_us_per_call(torch, fn, n=200):
+    """Host time for one call to return (argument checks, marshalling and the
+    enqueue; nothing synchronizes inside), median over n calls, in us."""
+    import numpy as np
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+    return round(1e6 * float(np.median(ts)), 2)
+
+
 def cpu_baseline(s, seconds, min_reps=3, max_reps=100000):
     """The oracle as it stands (single-threaded scalar C) on the same inputs:
     whole steps, repeated until about `seconds` of CPU time (at least
@@ -539,6 +553,13 @@ def main():
             pd()
             pc()
         prep_us = 1e6 * timed(moe, torch, sd, 500, 50, fn=step_prepared) / 500
+        host_calls = {
+            "dispatch": host_us_per_call(torch, lambda: moe.moe_dispatch(
+                sd["ctx"], sd["x"], sd["idx"], reuse_layout=False, bufs=sd["bufs"], handle=sd["h"])),
+            "combine": host_us_per_call(torch, lambda: moe.moe_combine(sd["ctx"], sd["y"], sd["w"], sd["h"],
+                                                                         out=sd["out"])),
+            "dispatch_prepared": host_us_per_call(torch, pd),
+            "combine_prepared": host_us_per_call(torch, pc)}
         cold = {n: 1e3 * kt_d[n]["total_ms"] / kt_d[n]["launches"] for n in ("dispatch", "combine")}
         cold_pct = {n: percentiles_us(kt_d[n]["ms"]) for n in ("dispatch", "combine")}
         cold_read_pct = {n: percentiles_us(kt_dr[n]["ms"]) for n in ("dispatch", "combine")}
@@ -548,6 +569,7 @@ def main():
             "us_per_step_warm": round(warm_us, 2),
             "us_per_step_graph": round(graph_us, 2),
             "us_per_step_prepared_calls": round(prep_us, 2),
+            "host_us_per_call": host_calls,
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
             "us_per_kernel_cold_p10_p50_p90": cold_pct,
             "us_per_kernel_cold_read_p10_p50_p90": cold_read_pct,

@@ -127,23 +127,28 @@ def _check(status, what):
         raise MoeError(status, what)
 
 
+# Pointers and stream handles go to the C calls as plain ints (or None for
+# NULL): ctypes converts them for c_void_p parameters, which costs less host
+# time per call than building c_void_p objects.
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
 
 
-# torch's raw current-stream query: ~0.1 us against ~2.7 us for building a
-# torch.cuda.Stream object per call (half of an eager decode step's host time
-# otherwise); the public API is the fallback where the query is missing
+# torch's raw current-stream and device queries: ~0.1 us against ~2.7 us for
+# building a torch.cuda.Stream object per call (half of an eager decode step's
+# host time otherwise); the public API is the fallback where they are missing
 _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
 
 
 def _stream(stream=None):
-    """HIP stream handle of a torch stream (default: the current stream)."""
+    """HIP stream handle (an int; 0 = the null stream) of a torch stream
+    (default: the current stream)."""
     if stream is None:
         if _raw_current_stream is not None:
-            return ctypes.c_void_p(_raw_current_stream(torch.cuda.current_device()))
+            return _raw_current_stream(_raw_device())
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
 def make_config(max_tokens, hidden, num_experts, num_ranks, topk, src_rank=0,
@@ -292,13 +297,13 @@ class DispatchBuffers:
                             if fp8 and not ll else None)
         self.recv_rows = torch.empty((n_recv, row_w), dtype=row_dt, device=dev)
         self.recv_scales = torch.empty((n_recv, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-        self.c = moe_dispatch_buffers(_ptr(self.send_rows).value, _ptr(self.send_scales).value,
-                                      _ptr(self.recv_rows).value, _ptr(self.recv_scales).value)
+        self.c = moe_dispatch_buffers(_ptr(self.send_rows), _ptr(self.send_scales),
+                                      _ptr(self.recv_rows), _ptr(self.recv_scales))
 
 
 # ---------------------------------------------------------------- the calls
 def _as_dev(t, dtype, name):
-    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+    if not (t.is_cuda and t.dtype is dtype and t.is_contiguous()):
         raise TypeError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
     return t
 
@@ -382,8 +387,9 @@ def moe_dispatch(ctx, x, topk_idx, reuse_layout=False, bufs=None, handle=None):
     c = ctx.cfg
     _as_dev(x, torch.bfloat16, "x")
     _as_dev(topk_idx, torch.int64, "topk_idx")
-    T = x.shape[0]
-    if x.dim() != 2 or x.shape[1] != c.hidden or tuple(topk_idx.shape) != (T, c.topk):
+    xs = x.shape
+    T = xs[0]
+    if len(xs) != 2 or xs[1] != c.hidden or topk_idx.shape != (T, c.topk):
         raise ValueError("x must be [T, %d] and topk_idx [T, %d]" % (c.hidden, c.topk))
     if bufs is None:
         bufs = DispatchBuffers(ctx)
@@ -403,7 +409,7 @@ def moe_combine(ctx, expert_out, topk_weights, handle, out=None):
     _as_dev(expert_out, torch.bfloat16, "expert_out")
     _as_dev(topk_weights, torch.float32, "topk_weights")
     T = handle.num_tokens
-    if tuple(topk_weights.shape) != (T, c.topk):
+    if topk_weights.shape != (T, c.topk):
         raise ValueError("topk_weights must be [T, %d]" % c.topk)
     if expert_out.numel() * 2 < ctx.hint(MOE_BUF_EXPERT_OUT):
         raise ValueError("expert_out smaller than MOE_BUF_EXPERT_OUT")

@@ -96,3 +96,20 @@ def test_cpu_baseline_runs_whole_steps_for_the_time_asked():
     assert runs == 3 and med > 0 and total >= med
     med, runs, total = bench.cpu_baseline(s, 0.2)
     assert total >= 0.2 and runs > 3 and med <= total
+
+
+def test_host_time_per_call_is_the_median_call():
+    """host_us_per_call times each call alone (no synchronization inside) and
+    reports the median in microseconds."""
+    import time
+    import types
+    syncs = []
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(synchronize=lambda: syncs.append(1)))
+    calls = []
+
+    def fn():
+        calls.append(1)
+        time.sleep(0.002 if len(calls) % 10 == 0 else 0.0)   # a few slow outliers
+    us = bench.host_us_per_call(fake_torch, fn, n=50)
+    assert len(calls) == 50 and len(syncs) == 2
+    assert 0 < us < 1000                       # the median ignores the 2 ms outliers

@@ -690,8 +690,9 @@ def test_current_stream_handle(gpu):
     and inside a side-stream context."""
     from combine_moe_dispatch_layout_amd import _binding as B
 
-    def handle(s):                       # c_void_p(0).value is None: the null stream
-        return s.value or 0
+    def handle(s):                       # an int; 0 is the null stream
+        assert isinstance(s, int)
+        return s
     assert handle(B._stream()) == torch.cuda.current_stream().cuda_stream
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
