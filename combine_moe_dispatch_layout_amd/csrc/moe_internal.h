@@ -17,6 +17,15 @@ constexpr int kCombineThreads = 64;
 
 // The fused low-latency dispatch handles up to this many (token, slot) entries
 // and tokens.
+// Layouts of at most this many 256-token tiles publish per-tile counts
+// column by column ([column][tile]) for the dispatch to sum (a few 16-byte
+// loads); larger ones publish them tile by tile ([tile][column]) and the last
+// layout block turns them into prefixes over the tiles, so that the dispatch
+// reads one value per column at any size.  Measured on MI355X: the sums are
+// faster up to 16384 tokens (by ~1 us per step at 4096 and 1-2% of a dispatch
+// after a cache flush), the stored prefixes make the dispatch 13% and 29%
+// faster at 32768 and 65536 tokens.
+constexpr int kWalkTiles = 64;
 constexpr int kFusedMaxEntries = 2048;
 constexpr int kFusedMaxTokens = 512;
 
@@ -35,8 +44,11 @@ struct LayoutArgs {
     uint32_t k_magic;          // ceil(2^20 / k):  entry -> token division
     uint32_t el_magic;         // ceil(2^20 / El): expert -> rank division
     int32_t max_tokens;        // row stride of srank
-    int32_t* tile_cnt;         // [E + R, tile_stride]  per-tile counts, transposed
+    int32_t* tile_cnt;         // up to kWalkTiles tiles: [E + R, tile_stride] per-tile counts;
+                               // beyond: [tiles, cnt_stride], rewritten by the last block as
+                               // exclusive prefixes over the tiles
     int32_t tile_stride;       // >= number of tiles, multiple of 4
+    int32_t cnt_stride;        // >= E + R, multiple of 64
     int32_t* grand_tot;        // [E + R]  totals over tiles (atomics; zero between launches)
     uint16_t* erank;           // [T, k]       rank of slot (t, j) among its expert's rows in the tile
     uint16_t* srank;           // [R, max_tokens] rank of token t among the tile's tokens sent to r
@@ -61,8 +73,9 @@ struct PackArgs {
     int32_t max_tokens;
     int32_t s0;
     int64_t cap;               // low-latency slots per expert (M * R)
-    const int32_t* tile_cnt;   // [E + R, tile_stride] per-tile counts, transposed
+    const int32_t* tile_cnt;   // per-tile counts or prefixes over the tiles (see LayoutArgs)
     int32_t tile_stride;
+    int32_t cnt_stride;
     const uint16_t* erank;
     const uint16_t* srank;
     const int32_t* cnt_e;

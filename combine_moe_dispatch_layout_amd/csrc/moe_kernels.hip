@@ -9,8 +9,9 @@
 //    (the lanes holding one expert find each other) plus per-wavefront LDS
 //    histograms -- no atomic decides any order, so results are deterministic.
 //    The last tile block to arrive (device-scope counter) scans the tile
-//    totals into global row bases, so count and scan are one launch; each
-//    block arrives before writing its in-tile ranks, overlapping the two.
+//    totals into global row bases (and, for large batches, turns the per-tile
+//    counts into prefixes over the tiles), so count and scan are one launch;
+//    each block arrives before writing its in-tile ranks, overlapping the two.
 //  * Dispatch: one wavefront per (token, row slice).  The slice is loaded once
 //    into registers with 16-byte loads, optionally quantised to E4M3 in
 //    registers (block amax by cross-lane max over the 16 lanes holding one
@@ -238,12 +239,14 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     __syncthreads();
 
     // ---- per-wavefront rank counts; exclusive prefixes over the wavefronts;
-    // tile totals: kept in LDS for a single tile, else published (transposed
-    // per-tile counts for the dispatch kernel's tile prefixes, plus atomic
-    // grand totals for the last block)
+    // tile totals: kept in LDS for a single tile; up to kWalkTiles tiles
+    // published column by column for the dispatch kernel to sum, plus atomic
+    // grand totals for the last block; beyond, published tile by tile with
+    // device-scope exchanges for the last block to read back
     for (int i = tid; i < kLayoutWaves * R; i += kLayoutThreads) hist_r[i] = __popcll(rank_toks[i]);
     __syncthreads();
-    int seen = 0;   // returned totals: using them makes the adds complete before the arrival below
+    const bool walk = ntiles <= kWalkTiles;
+    int seen = 0;   // returned values: using them makes the atomics complete before the arrival below
     for (int col = tid; col < E + R; col += kLayoutThreads) {
         const bool is_e = col < E;
         int32_t* h = is_e ? hist_e + col : hist_r + (col - E);
@@ -257,12 +260,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
         }
         if (ntiles == 1) {
             tot[col] = run;
-        } else {
+        } else if (walk) {
             a.tile_cnt[(int64_t)col * a.tile_stride + blockIdx.x] = run;
             if (run != 0) seen |= atomicAdd(&a.grand_tot[col], run);
+        } else {
+            seen |= __hip_atomic_exchange(&a.tile_cnt[(int64_t)blockIdx.x * a.cnt_stride + col], run,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (seen == -1) s_last = 2;   // never true: consumes the returned totals before the arrival
+    if (seen == -1) s_last = 2;   // never true (counts are >= 0): consumes the returned values before the arrival
     __syncthreads();
     // ---- arrival (see below), issued now so that its round trip overlaps phase 2
     unsigned arrived = 0u;
@@ -294,19 +300,46 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
         }
     }
 
-    // ---- arrival: the last block reads (and resets) the grand totals.  Only
-    // device-scope atomics cross blocks here (the totals, read back with atomic
-    // loads, and the arrival counter); each block's adds have completed (their
-    // returned values were consumed before the barrier ahead of its arrival),
-    // so no memory fence is needed -- on this chip a device-scope release fence
+    // ---- arrival: the last block reads (and resets) the grand totals, or
+    // (beyond kWalkTiles tiles) sums every column's per-tile counts into its
+    // total and rewrites them in place as exclusive prefixes over the tiles --
+    // one thread per column, consecutive columns in a wavefront's lanes, so
+    // each load and store covers a contiguous stretch of one tile's row; a
+    // batch of loads is issued before any is used.  Only device-scope atomics
+    // cross blocks here (the totals or counts, read back with atomic loads, and
+    // the arrival counter); each block's atomics have completed (their returned
+    // values were consumed before the barrier ahead of its arrival), so no
+    // memory fence is needed -- on this chip a device-scope release fence
     // writes back the whole L2.
     if (ntiles > 1) {
         if (tid == 0) s_last = (arrived == (unsigned)ntiles - 1);
         __syncthreads();
         if (!s_last) return;
-        for (int col = tid; col < E + R; col += kLayoutThreads) {
-            tot[col] = __hip_atomic_load(&a.grand_tot[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a.grand_tot[col] = 0;
+        if (walk) {
+            for (int col = tid; col < E + R; col += kLayoutThreads) {
+                tot[col] = __hip_atomic_load(&a.grand_tot[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                a.grand_tot[col] = 0;
+            }
+        } else {
+            constexpr int kBatch = 32;
+            for (int col = tid; col < E + R; col += kLayoutThreads) {
+                int32_t* p = a.tile_cnt + col;
+                int run = 0;
+                for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+                    int32_t c[kBatch];
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u)
+                        c[u] = t0 + u < ntiles ? __hip_atomic_load(p + (int64_t)(t0 + u) * a.cnt_stride,
+                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                               : 0;
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u) {
+                        if (t0 + u < ntiles) p[(int64_t)(t0 + u) * a.cnt_stride] = run;
+                        run += c[u];
+                    }
+                }
+                tot[col] = run;
+            }
         }
         __syncthreads();
     }
@@ -449,11 +482,18 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
     const int r = e >= 0 ? e / a.El : 0;
     const uint64_t peers = match_any(r, e >= 0, a.rbits);
     const bool first_of_rank = e >= 0 && (peers & below) == 0;
-    // rows of this expert (and tokens of this rank) in earlier tiles
+    // rows of this expert (and tokens of this rank) in earlier tiles: the sum
+    // of their per-tile counts, or beyond kWalkTiles tiles the layout kernel's
+    // prefix over the tiles
     int pre_e = 0, pre_r = 0;
     if (e >= 0 && tile > 0) {
-        pre_e = tile_prefix(a.tile_cnt + (int64_t)e * a.tile_stride, tile);
-        if (SEND && first_of_rank) pre_r = tile_prefix(a.tile_cnt + (int64_t)(a.E + r) * a.tile_stride, tile);
+        if ((int64_t)a.T <= (int64_t)kWalkTiles * kTileTokens) {
+            pre_e = tile_prefix(a.tile_cnt + (int64_t)e * a.tile_stride, tile);
+            if (SEND && first_of_rank) pre_r = tile_prefix(a.tile_cnt + (int64_t)(a.E + r) * a.tile_stride, tile);
+        } else {
+            pre_e = a.tile_cnt[(int64_t)tile * a.cnt_stride + e];
+            if (SEND && first_of_rank) pre_r = a.tile_cnt[(int64_t)tile * a.cnt_stride + a.E + r];
+        }
     }
     int cpos = -1;   // contiguous expert-major row (index into recv_src_idx)
     int rrow = -1;   // receive row (contiguous, or padded low-latency slot)

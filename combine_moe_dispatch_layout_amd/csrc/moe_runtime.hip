@@ -78,6 +78,8 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int tile_stride(const Geometry& g) { return (g.ntiles_max + 3) & ~3; }
 
+int cnt_stride(const moe_config* c) { return (c->num_experts + c->num_ranks + 63) & ~63; }
+
 Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     Workspace w;
     size_t o = 0;
@@ -88,7 +90,9 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     w.off_cnt_r = take(4 * (size_t)c->num_ranks);
     w.off_eoff = take(4 * ((size_t)c->num_experts + 1));
     w.off_roff = take(4 * ((size_t)c->num_ranks + 1));
-    w.off_tile_cnt = take(4 * (size_t)tile_stride(g) * (c->num_experts + c->num_ranks));
+    // per-tile counts in either arrangement (column by column, or tile by tile)
+    w.off_tile_cnt = take(4 * std::max((size_t)tile_stride(g) * (c->num_experts + c->num_ranks),
+                                       (size_t)g.ntiles_max * cnt_stride(c)));
     w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
     w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
@@ -212,6 +216,7 @@ moe_status run_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t T, int32_t*
     a.max_tokens = c.max_tokens;
     a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
     a.tile_stride = tile_stride(ctx->g);
+    a.cnt_stride = cnt_stride(&ctx->cfg);
     a.grand_tot = ctx->i32(ctx->wl.off_grand_tot);
     a.erank = ctx->u16(ctx->wl.off_erank);
     a.srank = ctx->u16(ctx->wl.off_srank);
@@ -463,6 +468,7 @@ MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk
     a.cap = ctx->g.cap;
     a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
     a.tile_stride = tile_stride(ctx->g);
+    a.cnt_stride = cnt_stride(&ctx->cfg);
     a.erank = ctx->u16(ctx->wl.off_erank);
     a.srank = ctx->u16(ctx->wl.off_srank);
     a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
