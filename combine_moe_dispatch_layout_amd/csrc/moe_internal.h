@@ -23,7 +23,7 @@ constexpr int kCombineThreads = 64;
 // layout block turns them into prefixes over the tiles, so that the dispatch
 // reads one value per column at any size.  Measured on MI355X: the sums are
 // faster up to 16384 tokens (by ~1 us per step at 4096 and 1-2% of a dispatch
-// after a cache flush), the stored prefixes make the dispatch 13% and 29%
+// after a cache flush), the stored prefixes make the dispatch 12% and 28%
 // faster at 32768 and 65536 tokens.
 constexpr int kWalkTiles = 64;
 constexpr int kFusedMaxEntries = 2048;

@@ -56,15 +56,18 @@ def poison(bufs):
 
 
 def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, check_poison=True,
-             tag="", max_workgroups=0, side_stream=False, tune=None):
-    """Layout + dispatch + combine on the GPU and in the oracle; compare all."""
+             tag="", max_workgroups=0, side_stream=False, tune=None, ctx=None):
+    """Layout + dispatch + combine on the GPU and in the oracle; compare all.
+    ctx: an existing context to run on (kept open), else a fresh one."""
     T = idx.shape[0]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
     fp8 = c["quant"] == W.QUANT_FP8
     log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d max_wg=%d side=%s" %
         (tag, T, c["H"], c["E"], c["R"], c["k"], c["quant"], c["layout"], reuse, src_rank, max_workgroups,
          side_stream))
-    ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
+    own_ctx = ctx is None
+    if own_ctx:
+        ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
     if max_workgroups:
         ctx.set_max_workgroups(max_workgroups)
     if tune is not None:
@@ -173,7 +176,8 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     assert d.max(initial=0) <= 1, "combine beyond 1 bf16 ulp"
     assert n_diff == 0, "combine expected bit-exact (separately rounded fp32 multiply and add)"
     del y
-    ctx.close()
+    if own_ctx:
+        ctx.close()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return ref
@@ -748,6 +752,28 @@ def test_many_tiles(gpu, quant):
     x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
     w = W.softmax_weights(rng, T, c["k"])
     run_case(gpu, c, x, idx, w, max_tokens=T, tag="many-tiles-q%d" % quant)
+
+
+@pytest.mark.parametrize("T,layout,reuse", [(16384, W.LAYOUT_CONTIGUOUS, True), (16385, W.LAYOUT_CONTIGUOUS, True),
+                                            (16385, W.LAYOUT_CONTIGUOUS, False), (20000, W.LAYOUT_PADDED_LL, True),
+                                            (16384, W.LAYOUT_PADDED_LL, False)])
+def test_tile_prefix_boundary(gpu, T, layout, reuse):
+    """Both sides of the size where the layout stops leaving per-tile counts
+    for the dispatch to sum (64 tiles, 16,384 tokens) and stores prefixes over
+    the tiles instead; normal and low-latency layouts, layout reused or not,
+    empty slots; then a smaller batch on the same context, which must not see
+    the larger one's workspace contents."""
+    c = dict(index=22, T=T, H=128, E=64, R=8, k=6, quant=W.QUANT_BF16, layout=layout, max_tokens=T)
+    rng = np.random.Generator(np.random.PCG64(T + 7 * layout))
+    idx = W.with_empty_slots(W.route_uniform(rng, T, c["E"], c["k"]), 0.05, seed=11)
+    x = W.to_bf16_bits(rng.standard_normal((T, c["H"]), dtype=np.float32))
+    w = W.softmax_weights(rng, T, c["k"])
+    ctx = make_ctx(gpu, c, T, max_tokens=T)
+    run_case(gpu, c, x, idx, w, reuse=reuse, max_tokens=T, tag="tile-boundary-%d" % T, ctx=ctx)
+    T2 = 5000
+    run_case(gpu, c, x[:T2].copy(), idx[:T2].copy(), w[:T2].copy(), reuse=reuse, max_tokens=T,
+             tag="tile-boundary-then-%d" % T2, ctx=ctx)
+    ctx.close()
 
 
 @pytest.mark.parametrize("T,reuse,quant", [(128, False, W.QUANT_FP8), (128, True, W.QUANT_BF16),
