@@ -351,12 +351,14 @@ def copy_reference(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (us * 1e-6) / 1e9
 
 
-def all_configs(moe, W, torch, flushes):
+def all_configs(moe, W, torch, flushes, with_oracle=True):
     """Warm step time and algorithmic GB/s of every workload (the layout-reusing
     step for the contiguous layout, the fused low-latency step for the padded one),
     and per kernel the p10/p50/p90 event durations warm and cold (caches flushed):
     10 warm-up steps, then 1000 timed steps for the two latency-bound workloads
-    and 100 for the others."""
+    and 100 for the others.  With `with_oracle`, also the oracle's step on the
+    same inputs on one host core (median of 101 steps for the two latency-bound
+    workloads, 3 for the others): a reported baseline, not a target."""
     out = {}
     for name in ("tiny", "decode", "prefill", "grouped", "skewed"):
         steps = 1000 if name in ("tiny", "decode") else 100
@@ -377,6 +379,10 @@ def all_configs(moe, W, torch, flushes):
                      "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                      "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
                      "steps": steps, "kernels": kernel_table(kt, alg, cold=kt_cold)}
+        if with_oracle:
+            runs = 101 if name in ("tiny", "decode") else 3
+            ms = oracle_step_ms(s, runs)
+            out[name]["oracle_cpu"] = {"ms_per_step": round(ms, 3), "runs": runs, "cores": 1}
         s["ctx"].close()
         del s
         torch.cuda.empty_cache()
@@ -408,6 +414,43 @@ def host_us_per_call(torch, fn, n=200):
         ts.append(time.perf_counter() - t0)
     torch.cuda.synchronize()
     return round(1e6 * float(np.median(ts)), 2)
+
+
+def oracle_step_ms(s, runs):
+    """The oracle's whole step on one workload, single-threaded scalar C pinned to
+    one host core: layout, positions and payload rows as the workload's mode
+    writes them (send rows and the contiguous receive layout, or the padded
+    low-latency rows), then the combine over the expert outputs the GPU step
+    reads.  Median of `runs` steps, in ms.  In the padded mode those outputs sit
+    at the oracle's own padded rows (`pos_ll`), gathered once, untimed, into the
+    oracle's expert-major order, so the combine sums the same values."""
+    import numpy as np
+    import oracle
+    import torch
+    d, c = s["d"], s["c"]
+    ll = c["layout"] == 1
+    kw = dict(quant=c["quant"], max_tokens=c["max_tokens"] if ll else 0, with_send=not ll)
+    ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], **kw)
+    pos = ref["pos"]
+    if ll:
+        valid = pos >= 0
+        src = torch.from_numpy(ref["pos_ll"][valid].astype(np.int64)).to(s["y"].device)
+        y = np.empty((ref["n_pairs"], c["H"]), np.uint16)
+        y[pos[valid]] = s["y"][src].cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        y = s["y"][:ref["n_pairs"]].cpu().view(torch.int16).numpy().view(np.uint16)
+    saved = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(saved)})
+    times = []
+    try:
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], **kw)
+            oracle.combine(y, d["topk_weights"], r["pos"])
+            times.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, saved)
+    return 1e3 * float(np.median(times))
 
 
 def cpu_baseline(s, seconds, min_reps=3, max_reps=100000):
@@ -586,7 +629,7 @@ def main():
                                   "dominant_kernel_frac_of_copy": round(achieved / cp, 3)}
 
     if not a.profile_only and not a.no_configs and a.step == "forward":
-        line["configs"] = all_configs(moe, W, torch, flushes)
+        line["configs"] = all_configs(moe, W, torch, flushes, with_oracle=not a.no_cpu_baseline)
 
     if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
         model, ncpu = host_cpu()

@@ -113,3 +113,36 @@ def test_host_time_per_call_is_the_median_call():
     us = bench.host_us_per_call(fake_torch, fn, n=50)
     assert len(calls) == 50 and len(syncs) == 2
     assert 0 < us < 1000                       # the median ignores the 2 ms outliers
+
+
+def test_oracle_step_per_workload_in_both_receive_modes(monkeypatch):
+    """The per-workload oracle time runs whole oracle steps (the requested
+    number, pinned to one core and then unpinned), in the contiguous mode and in
+    the padded low-latency mode; in the padded mode the combine reads the
+    expert outputs at the oracle's own padded rows."""
+    import torch
+    d = W.make("tiny")
+    c = d["cfg"]
+    ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
+    n = ref["n_pairs"]
+    y = torch.from_numpy(W.expert_outputs(d, n).view(np.int16)).view(torch.bfloat16)
+    before = os.sched_getaffinity(0)
+    assert bench.oracle_step_ms({"d": d, "c": c, "y": y}, 3) > 0
+    assert os.sched_getaffinity(0) == before
+
+    # the same tokens in the padded layout: expert outputs at e * cap + slot
+    cl = dict(c, layout=1, max_tokens=c["T"])
+    cap = cl["max_tokens"] * c["R"]
+    ll = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"], max_tokens=cl["max_tokens"],
+                         with_send=False)
+    valid = ll["pos"] >= 0
+    y_pad = torch.zeros((c["E"] * cap, c["H"]), dtype=torch.bfloat16)
+    y_pad[torch.from_numpy(ll["pos_ll"][valid].astype(np.int64))] = y[torch.from_numpy(
+        ll["pos"][valid].astype(np.int64))]
+    combined = []
+    real_combine = oracle.combine
+    monkeypatch.setattr(oracle, "combine", lambda yy, w, pos: combined.append(real_combine(yy, w, pos)))
+    assert bench.oracle_step_ms({"d": d, "c": cl, "y": y_pad}, 2) > 0
+    assert len(combined) == 2
+    expect = real_combine(y.view(torch.int16).numpy().view(np.uint16), d["topk_weights"], ref["pos"])
+    assert all(np.array_equal(o, expect) for o in combined)
