@@ -10,11 +10,16 @@ virtual ranks, top-8, bf16 dispatch into per-rank send buffers and the
 expert-major receive layout, bf16 combine.  Inputs are resident in HBM before
 the timed region; nothing is allocated inside it.
 
-value = algorithmic HBM bytes of one step (x read once, every destination row
-written once, expert outputs read once, outputs written once, routing
-metadata) / measured time per step, in GB/s.  The per-kernel roofline uses
+Headline protocol ("cold"): before every step, warm-up and timed alike, a
+1 GiB buffer (4x the 256 MB Infinity Cache) is rewritten, untimed, so that
+each step starts with the L2 and the Infinity Cache holding none of its data;
+each timed step is bracketed by HIP events on the stream the library launches
+on.  value = algorithmic HBM bytes of one step (x read once, every
+destination row written once, expert outputs read once, outputs written once,
+routing metadata) / mean cold step time, in GB/s.  The same steps back to back
+with no flush ("warm") are reported beside it.  The per-kernel roofline uses
 durations measured with HIP events the library records on its own launch
-stream around each kernel (moe_timing_begin / moe_timing_end).
+stream around each kernel (moe_timing_begin / moe_timing_end), cold.
 
 Prints ONE JSON line.  --gpus N with N > 1 is refused: this build drives one GPU.
 """
@@ -131,6 +136,32 @@ def kernel_table(kt, alg, cold=None):
     return out
 
 
+def kernel_passes(passes, alg, primary):
+    """Per kernel, for each pass ({label: timings}): mean event duration,
+    algorithmic GB/s on it and on the median, p10/p50/p90 of the launches;
+    "us" and "GB/s" repeat the primary pass's figures."""
+    import numpy as np
+    out = {}
+    for name, b in alg.items():
+        if b == 0 or passes[primary][name]["launches"] == 0:
+            continue
+        ent = {"alg_bytes": b}
+        for lb, kt in passes.items():
+            n = kt[name]["launches"]
+            if n == 0:
+                continue
+            us = 1e3 * kt[name]["total_ms"] / n
+            p50 = float(np.median(1e3 * np.asarray(kt[name]["ms"], dtype=np.float64)))
+            ent["us_" + lb] = round(us, 2)
+            ent["GB/s_" + lb] = round(b / (us * 1e-6) / 1e9, 1)
+            ent["GB/s_%s_p50" % lb] = round(b / (p50 * 1e-6) / 1e9, 1)
+            ent["us_%s_p10_p50_p90" % lb] = percentiles_us(kt[name]["ms"])
+        ent["us"] = ent["us_" + primary]
+        ent["GB/s"] = ent["GB/s_" + primary]
+        out[name] = ent
+    return out
+
+
 def setup(moe, W, torch, name, T=None):
     d = W.make(name, T=T)
     c = d["cfg"]
@@ -227,6 +258,37 @@ def timed_graph(moe, torch, s, fn, steps_per_graph=100, replays=10):
     assert st == moe.MOE_OK, st
     del g
     return wall / (replays * steps_per_graph)
+
+
+def timed_cold(moe, torch, s, steps, warmup, flush, fn=step):
+    """The headline protocol: `warmup` then `steps` steps, each preceded by
+    `flush` (untimed); each timed step is bracketed by events on the current
+    stream, where the library launches.  Returns (per-step ms, wall seconds
+    of the whole timed loop, flushes included)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(warmup):
+        flush()
+        fn(moe, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        ev[i][0].record()
+        fn(moe, s)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st, _ = moe.moe_poll_error(s["ctx"])
+    assert st == moe.MOE_OK, st
+    return [e0.elapsed_time(e1) for e0, e1 in ev], wall
+
+
+def make_flushes(torch):
+    """Cache flushes run before a step: "cold" rewrites a 1 GiB buffer (the
+    headline protocol; its dirty lines are written back while the step runs),
+    "cold_read" only reads it (evicts without leaving dirty lines)."""
+    fbuf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    return {"cold": lambda: fbuf.add_(1), "cold_read": lambda: fbuf.sum()}
 
 
 def timed_kernels(moe, torch, s, steps, flush=None, fn=step):
@@ -352,12 +414,14 @@ def copy_reference(torch, nbytes=1 << 30, reps=20):
 
 
 def all_configs(moe, W, torch, flushes, with_oracle=True):
-    """Warm step time and algorithmic GB/s of every workload (the layout-reusing
-    step for the contiguous layout, the fused low-latency step for the padded one),
-    and per kernel the p10/p50/p90 event durations warm and cold (caches flushed):
-    10 warm-up steps, then 1000 timed steps for the two latency-bound workloads
-    and 100 for the others.  With `with_oracle`, also the oracle's step on the
-    same inputs on one host core (median of 101 steps for the two latency-bound
+    """Per workload (the layout-reusing step for the contiguous layout, the
+    fused low-latency step for the padded one): the step time and algorithmic
+    GB/s cold (the headline protocol, a 1 GiB write flush before each step)
+    and warm (back to back), and per kernel the p10/p50/p90 event durations
+    warm and cold: 10 warm-up steps, then 1000 timed steps for the two
+    latency-bound workloads and 100 for the others.  With `with_oracle`, also
+    the oracle on the same inputs on one host core, layout, dispatch and
+    combine timed separately (medians of 101 steps for the two latency-bound
     workloads, 3 for the others): a reported baseline, not a target."""
     out = {}
     for name in ("tiny", "decode", "prefill", "grouped", "skewed"):
@@ -371,18 +435,23 @@ def all_configs(moe, W, torch, flushes, with_oracle=True):
             fn = step_ll
             alg["layout"] = 0
         us = 1e6 * timed(moe, torch, s, steps, 10, fn=fn) / steps
+        cold_ms, _ = timed_cold(moe, torch, s, steps, 10, flushes["cold"], fn=fn)
+        us_cold = 1e3 * sum(cold_ms) / len(cold_ms)
         kt = timed_kernels(moe, torch, s, steps, fn=fn)
         kt_cold = {lb: timed_kernels(moe, torch, s, steps, flush=f, fn=fn) for lb, f in flushes.items()}
         b = sum(alg.values())
         out[name] = {"T": T, "H": c["H"], "E": c["E"], "R": c["R"], "k": c["k"],
                      "mode": ("fp8 " if c["quant"] else "bf16 ") + ("padded-LL" if c["layout"] else "send+contiguous"),
+                     "us_per_step_cold": round(us_cold, 2),
+                     "us_per_step_cold_p10_p50_p90": percentiles_us(cold_ms),
+                     "GB/s_cold": round(b / (us_cold * 1e-6) / 1e9, 1),
+                     "pct_of_hbm_peak_cold": round(100 * b / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
                      "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                      "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
                      "steps": steps, "kernels": kernel_table(kt, alg, cold=kt_cold)}
         if with_oracle:
             runs = 101 if name in ("tiny", "decode") else 3
-            ms = oracle_step_ms(s, runs)
-            out[name]["oracle_cpu"] = {"ms_per_step": round(ms, 3), "runs": runs, "cores": 1}
+            out[name]["oracle_cpu"] = dict(oracle_timing(s, runs=runs), cores=1)
         s["ctx"].close()
         del s
         torch.cuda.empty_cache()
@@ -416,14 +485,11 @@ def host_us_per_call(torch, fn, n=200):
     return round(1e6 * float(np.median(ts)), 2)
 
 
-def oracle_step_ms(s, runs):
-    """The oracle's whole step on one workload, single-threaded scalar C pinned to
-    one host core: layout, positions and payload rows as the workload's mode
-    writes them (send rows and the contiguous receive layout, or the padded
-    low-latency rows), then the combine over the expert outputs the GPU step
-    reads.  Median of `runs` steps, in ms.  In the padded mode those outputs sit
-    at the oracle's own padded rows (`pos_ll`), gathered once, untimed, into the
-    oracle's expert-major order, so the combine sums the same values."""
+def oracle_inputs(s):
+    """What the oracle's combine reads: the expert outputs the GPU step reads,
+    in the oracle's expert-major order.  In the padded mode those outputs sit
+    at the oracle's own padded rows (`pos_ll`), gathered once, untimed, into
+    its expert-major order, so that the combine sums the same values."""
     import numpy as np
     import oracle
     import torch
@@ -439,39 +505,51 @@ def oracle_step_ms(s, runs):
         y[pos[valid]] = s["y"][src].cpu().view(torch.int16).numpy().view(np.uint16)
     else:
         y = s["y"][:ref["n_pairs"]].cpu().view(torch.int16).numpy().view(np.uint16)
-    saved = os.sched_getaffinity(0)
-    os.sched_setaffinity(0, {min(saved)})
-    times = []
-    try:
-        for _ in range(runs):
-            t0 = time.perf_counter()
-            r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], **kw)
-            oracle.combine(y, d["topk_weights"], r["pos"])
-            times.append(time.perf_counter() - t0)
-    finally:
-        os.sched_setaffinity(0, saved)
-    return 1e3 * float(np.median(times))
+    return y, kw
 
 
-def cpu_baseline(s, seconds, min_reps=3, max_reps=100000):
-    """The oracle as it stands (single-threaded scalar C) on the same inputs:
-    whole steps, repeated until about `seconds` of CPU time (at least
-    min_reps).  Returns (median seconds per step, steps run, total seconds)."""
-    import numpy as np
+def oracle_ops(s, y, kw):
+    """One oracle step, each op timed on its own (seconds): layout; positions
+    and payload rows (the dispatch); combine."""
     import oracle
     d, c = s["d"], s["c"]
-    # one host core, like the single-threaded oracle it times
+    t0 = time.perf_counter()
+    lay = oracle.layout(d["topk_idx"], c["E"], c["R"])
+    t1 = time.perf_counter()
+    pp = oracle.positions(d["topk_idx"], c["E"], c["R"], lay, kw["max_tokens"])
+    oracle.rows(d["x"], pp, kw["quant"], kw["with_send"])
+    t2 = time.perf_counter()
+    oracle.combine(y, d["topk_weights"], pp["pos"])
+    t3 = time.perf_counter()
+    return t1 - t0, t2 - t1, t3 - t2
+
+
+def oracle_timing(s, runs=None, seconds=None, min_runs=3, max_runs=100000):
+    """The oracle (single-threaded scalar C) on one workload, pinned to one host
+    core: layout, dispatch (positions + payload rows as the workload's mode
+    writes them) and combine, each timed on its own, over `runs` steps or
+    until about `seconds` of CPU time (at least min_runs).  Returns the medians
+    in ms and the number of steps run."""
+    import numpy as np
+    y, kw = oracle_inputs(s)
     saved = os.sched_getaffinity(0)
     os.sched_setaffinity(0, {min(saved)})
-    y = s["y"][:s["n_pairs"]].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
-    times = []
-    while len(times) < min_reps or (sum(times) < seconds and len(times) < max_reps):
-        t0 = time.perf_counter()
-        r = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
-        oracle.combine(y, d["topk_weights"], r["pos"])
-        times.append(time.perf_counter() - t0)
-    os.sched_setaffinity(0, saved)
-    return float(np.median(times)), len(times), float(sum(times))
+    per = []
+    try:
+        while True:
+            per.append(oracle_ops(s, y, kw))
+            n = len(per)
+            if runs is not None and n >= runs:
+                break
+            if runs is None and n >= min_runs and (sum(map(sum, per)) >= seconds or n >= max_runs):
+                break
+    finally:
+        os.sched_setaffinity(0, saved)
+    a = 1e3 * np.asarray(per)
+    return {"layout_ms": round(float(np.median(a[:, 0])), 4), "dispatch_ms": round(float(np.median(a[:, 1])), 4),
+            "combine_ms": round(float(np.median(a[:, 2])), 4),
+            "step_ms": round(float(np.median(a.sum(axis=1))), 4), "runs": len(per),
+            "cpu_seconds": round(float(a.sum()) / 1e3, 2)}
 
 
 def main():
@@ -513,23 +591,27 @@ def main():
         step_desc = ("dispatch from topk_idx (fused) + combine" if fn is step_ll
                      else "layout + dispatch(reuse layout) + combine")
     step_bytes = sum(alg.values())
-    wall = timed(moe, torch, s, a.steps, a.warmup, fn=fn)
-    kt = timed_kernels(moe, torch, s, a.steps, fn=fn)
-    ms_per_step = 1e3 * wall / a.steps
-    value = step_bytes / (wall / a.steps) / 1e9
-
-    # the same steps with the caches flushed before each one by a 1 GiB buffer (4x the Infinity
-    # Cache): "cold" rewrites it (its dirty lines are written back during the step), "cold_read"
-    # only reads it (evicts without leaving dirty lines)
-    flushes = {}
+    # the headline: W + K steps, each after a 1 GiB write flush, K of them timed with events
+    flushes = make_flushes(torch)
+    cold_ms, cold_wall = timed_cold(moe, torch, s, a.steps, a.warmup, flushes["cold"], fn=fn)
+    ms_per_step = sum(cold_ms) / len(cold_ms)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # per-kernel durations (library events), cold; warm (back to back) and after a read flush beside
+    passes = {"cold": timed_kernels(moe, torch, s, a.steps, flush=flushes["cold"], fn=fn)}
+    warm = None
     if not a.profile_only:
-        fbuf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
-        flushes = {"cold": lambda: fbuf.add_(1), "cold_read": lambda: fbuf.sum()}
-    cold_pass = lambda fn_, steps_: {lb: timed_kernels(moe, torch, s, steps_, flush=f, fn=fn_)
-                                     for lb, f in flushes.items()}
-    per_kernel = kernel_table(kt, alg, cold=cold_pass(fn, min(a.steps, 100)))
+        wall = timed(moe, torch, s, a.steps, a.warmup, fn=fn)
+        warm = {"ms_per_step": round(1e3 * wall / a.steps, 4),
+                "value": round(step_bytes / (wall / a.steps) / 1e9, 1),
+                "pct_of_hbm_peak": round(100 * step_bytes / (wall / a.steps) / 1e9 / HBM_PEAK_GBS, 1),
+                "what": "the same %d steps back to back, no flush, wall clock" % a.steps}
+        passes["warm"] = timed_kernels(moe, torch, s, a.steps, fn=fn)
+        passes["cold_read"] = timed_kernels(moe, torch, s, a.steps, flush=flushes["cold_read"], fn=fn)
+    per_kernel = kernel_passes(passes, alg, "cold")
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     achieved = per_kernel[dom]["GB/s"]
+    cold_pass = lambda fn_, steps_: {lb: timed_kernels(moe, torch, s, steps_, flush=f, fn=fn_)
+                                     for lb, f in flushes.items()}
 
     line = {
         "metric": "dispatch+combine us/call and HBM GB/s (% of peak), 128 & 4096 tok x 7168, top-8",
@@ -539,6 +621,11 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "protocol": "cold: a 1 GiB buffer rewritten (untimed) before every warm-up and timed step; "
+                    "per-step HIP events on the launch stream; value = bytes / mean step",
+        "us_per_step_p10_p50_p90": percentiles_us(cold_ms),
+        "timed_loop_s_with_flushes": round(cold_wall, 4),
+        "warm": warm,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -553,6 +640,14 @@ def main():
         "kernels": per_kernel,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "frac_cold": round(achieved / HBM_PEAK_GBS, 4),
+                     "achieved_cold_p50": per_kernel[dom]["GB/s_cold_p50"],
+                     "frac_cold_p50": round(per_kernel[dom]["GB/s_cold_p50"] / HBM_PEAK_GBS, 4),
+                     "achieved_warm": per_kernel[dom].get("GB/s_warm"),
+                     "frac_warm": (round(per_kernel[dom]["GB/s_warm"] / HBM_PEAK_GBS, 4)
+                                   if "GB/s_warm" in per_kernel[dom] else None),
+                     "alg_bytes_per_launch": per_kernel[dom]["alg_bytes"],
+                     "us_per_launch": per_kernel[dom]["us"],
                      "traffic": traffic_for(dom, a.workload + ("_backward" if a.step == "backward" else ""))},
     }
 
@@ -633,13 +728,18 @@ def main():
 
     if not a.profile_only and not a.no_cpu_baseline and a.step == "forward":
         model, ncpu = host_cpu()
-        sec, runs, total = cpu_baseline(s, a.cpu_seconds)
+        o = oracle_timing(s, seconds=a.cpu_seconds)
+        sec = o["step_ms"] * 1e-3
         line["cpu_baseline"] = {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle",
-                                "sample": "the full %s workload (%d tokens): layout, positions, payload "
-                                          "rows and combine in the scalar C oracle, median of %d runs "
-                                          "(%.2f s each, %.1f s in all), pinned to one of %d host cores "
-                                          "(%s)" % (a.workload, T, runs, sec, total, ncpu, model)}
+                                "layout_ms": o["layout_ms"], "dispatch_ms": o["dispatch_ms"],
+                                "combine_ms": o["combine_ms"], "step_ms": o["step_ms"],
+                                "cpu_model": model, "host_cores_visible": ncpu,
+                                "sample": "the full %s workload (%d tokens): layout, then positions and "
+                                          "payload rows (dispatch), then combine, each timed on its own in "
+                                          "the scalar C oracle; medians of %d steps (%.1f s of CPU in all), "
+                                          "pinned to one of %d host cores (%s)"
+                                          % (a.workload, T, o["runs"], o["cpu_seconds"], ncpu, model)}
     print(json.dumps(line), flush=True)
     s["ctx"].close()
 

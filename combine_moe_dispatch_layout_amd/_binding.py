@@ -22,6 +22,12 @@ MOE_ERR_HANDLE = 4
 MOE_ERR_HIP = 5
 MOE_ERR_BAD_TOPK = 6
 MOE_ERR_DEVICE_BOUNDS = 7
+MOE_ERR_STALE_LAYOUT = 8
+MOE_ERR_NONFINITE = 9
+# moe_poll_error's raw bits
+ERR_FLAG_BAD_TOPK, ERR_FLAG_BOUNDS, ERR_FLAG_CAPACITY, ERR_FLAG_STALE, ERR_FLAG_NONFINITE = 1, 2, 4, 8, 16
+_POLL_STATUSES = (MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY, MOE_ERR_DEVICE_BOUNDS, MOE_ERR_STALE_LAYOUT,
+                  MOE_ERR_NONFINITE)
 
 MOE_QUANT_BF16 = 0
 MOE_QUANT_FP8_E4M3 = 1
@@ -523,6 +529,6 @@ def moe_poll_error(ctx):
     """Synchronizes the current stream; returns (status, raw flags) and clears them."""
     flags = ctypes.c_uint32(0)
     st = load_library().moe_poll_error(ctx.handle, _stream(), ctypes.byref(flags))
-    if st not in (MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY, MOE_ERR_DEVICE_BOUNDS):
+    if st not in _POLL_STATUSES:
         raise MoeError(st, "moe_poll_error")
     return st, flags.value

@@ -37,6 +37,24 @@ constexpr int bwd_max_waves(int k) { return k > 8 ? 4 : 16; }
 constexpr uint32_t kErrBadTopk = 1u;
 constexpr uint32_t kErrBounds = 2u;
 constexpr uint32_t kErrCapacity = 4u;   // a low-latency slot window overflowed (row not placed)
+constexpr uint32_t kErrStale = 8u;      // a reused layout no longer matches topk_idx (token dropped)
+constexpr uint32_t kErrNonFinite = 16u; // fp8 dispatch met Inf or NaN in a 128-channel block
+
+// Layout mode, chosen on the host from the tile count and passed to both the
+// layout and the dispatch kernels (never re-derived on the device).
+constexpr int kLayoutOneTile = 0;   // a single tile: no per-tile counts at all
+constexpr int kLayoutWalk = 1;      // per-tile counts column by column, summed by the dispatch
+constexpr int kLayoutPrefix = 2;    // per-tile exclusive prefixes, tile by tile
+inline int layout_mode(int ntiles) {
+    return ntiles <= 1 ? kLayoutOneTile : (ntiles <= kWalkTiles ? kLayoutWalk : kLayoutPrefix);
+}
+
+// In-tile expert rank of a (token, slot) entry, with the entry's expert id in
+// the high half so that a dispatch reusing the layout can check that topk_idx
+// has not changed since (0xFFFF = empty or invalid slot).
+__host__ __device__ inline uint32_t erank_pack(int e, int rank) {
+    return e >= 0 ? ((uint32_t)e << 16) | (uint32_t)rank : 0xFFFF0000u;
+}
 
 struct LayoutArgs {
     const int64_t* topk_idx;   // [T, k]
@@ -44,13 +62,16 @@ struct LayoutArgs {
     uint32_t k_magic;          // ceil(2^20 / k):  entry -> token division
     uint32_t el_magic;         // ceil(2^20 / El): expert -> rank division
     int32_t max_tokens;        // row stride of srank
+    int32_t mode;              // kLayoutOneTile / kLayoutWalk / kLayoutPrefix (must match the grid)
+    int32_t in_rank_vec4;      // out_in_rank is 4-byte aligned and R % 4 == 0: 32-bit stores
     int32_t* tile_cnt;         // up to kWalkTiles tiles: [E + R, tile_stride] per-tile counts;
                                // beyond: [tiles, cnt_stride], rewritten by the last block as
                                // exclusive prefixes over the tiles
     int32_t tile_stride;       // >= number of tiles, multiple of 4
     int32_t cnt_stride;        // >= E + R, multiple of 64
     int32_t* grand_tot;        // [E + R]  totals over tiles (atomics; zero between launches)
-    uint16_t* erank;           // [T, k]       rank of slot (t, j) among its expert's rows in the tile
+    uint32_t* erank;           // [T, k]       erank_pack(expert, rank of slot (t, j) among the
+                               //              expert's rows in the tile)
     uint16_t* srank;           // [R, max_tokens] rank of token t among the tile's tokens sent to r
     int32_t* cnt_e;            // [E]   workspace copies of the results
     int32_t* cnt_r;            // [R]
@@ -76,7 +97,8 @@ struct PackArgs {
     const int32_t* tile_cnt;   // per-tile counts or prefixes over the tiles (see LayoutArgs)
     int32_t tile_stride;
     int32_t cnt_stride;
-    const uint16_t* erank;
+    int32_t mode;              // the layout mode the layout kernel ran with
+    const uint32_t* erank;
     const uint16_t* srank;
     const int32_t* cnt_e;
     const int32_t* eoff;

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     // device-scope exchanges for the last block to read back
     for (int i = tid; i < kLayoutWaves * R; i += kLayoutThreads) hist_r[i] = __popcll(rank_toks[i]);
     __syncthreads();
-    const bool walk = ntiles <= kWalkTiles;
+    const int mode = a.mode;   // matches the grid (chosen on the host from the tile count)
     int seen = 0;   // returned values: using them makes the atomics complete before the arrival below
     for (int col = tid; col < E + R; col += kLayoutThreads) {
         const bool is_e = col < E;
@@ -258,9 +258,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
             h[ww * stride] = run;
             run += c;
         }
-        if (ntiles == 1) {
+        if (mode == kLayoutOneTile) {
             tot[col] = run;
-        } else if (walk) {
+        } else if (mode == kLayoutWalk) {
             a.tile_cnt[(int64_t)col * a.tile_stride + blockIdx.x] = run;
             if (run != 0) seen |= atomicAdd(&a.grand_tot[col], run);
         } else {
@@ -272,13 +272,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     __syncthreads();
     // ---- arrival (see below), issued now so that its round trip overlaps phase 2
     unsigned arrived = 0u;
-    if (ntiles > 1 && tid == 0) arrived = atomicAdd(a.done, 1u);
+    if (mode != kLayoutOneTile && tid == 0) arrived = atomicAdd(a.done, 1u);
 
-    // ---- phase 2: tile-local ranks out
+    // ---- phase 2: tile-local ranks out, each with its expert id (every entry,
+    // empty ones too, so that a dispatch reusing the layout can check them)
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) {
-        if (c < nch && ev[c] >= 0)
-            a.erank[ent0 + (int64_t)c * 64 + lane] = (uint16_t)(hist_e[w * E + ev[c]] + erl[c]);
+        const int64_t i = (int64_t)c * 64 + lane;
+        if (c < nch && i < nent)
+            a.erank[ent0 + i] = erank_pack(ev[c], ev[c] >= 0 ? hist_e[w * E + ev[c]] + erl[c] : 0);
     }
     const uint64_t rmask = lane < kWaveTokens ? tok_mask[w * kWaveTokens + lane] : 0ull;   // 0 past T
     if (tok_ok) {
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
             a.srank[(int64_t)r * a.max_tokens + t] = (uint16_t)rk;
         }
         if (a.out_in_rank != nullptr) {
-            if ((R & 3) == 0) {   // 4 flags per 32-bit store
+            if (a.in_rank_vec4) {   // 4 flags per 32-bit store (aligned, R % 4 == 0)
                 uint32_t* dst = reinterpret_cast<uint32_t*>(a.out_in_rank + t * R);
                 for (int r = 0; r < R; r += 4) {
                     const uint32_t b = (uint32_t)(rmask >> r);
@@ -311,11 +313,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     // values were consumed before the barrier ahead of its arrival), so no
     // memory fence is needed -- on this chip a device-scope release fence
     // writes back the whole L2.
-    if (ntiles > 1) {
+    if (mode != kLayoutOneTile) {
         if (tid == 0) s_last = (arrived == (unsigned)ntiles - 1);
         __syncthreads();
         if (!s_last) return;
-        if (walk) {
+        if (mode == kLayoutWalk) {
             for (int col = tid; col < E + R; col += kLayoutThreads) {
                 tot[col] = __hip_atomic_load(&a.grand_tot[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 a.grand_tot[col] = 0;
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     if (tid == 0) {
         a.eoff[E] = total_e;
         a.roff[R] = total_r;
-        if (ntiles > 1) *a.done = 0u;
+        if (mode != kLayoutOneTile) *a.done = 0u;
     }
 }
 
@@ -449,6 +451,23 @@ __device__ __forceinline__ void quantize_slice(const u32x4* v, u32x2* q, float* 
     }
 }
 
+// Whether any bf16 value of a slice (C 16-byte chunks per lane) is Inf or NaN
+// (exponent bits all ones); the E4M3 codes of such a block are unspecified.
+template <int C>
+__device__ __forceinline__ bool slice_nonfinite(const u32x4* v) {
+    uint32_t bad = 0u;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            bad |= (w[u] & 0x7f80u) == 0x7f80u;
+            bad |= (w[u] & 0x7f800000u) == 0x7f800000u;
+        }
+    }
+    return bad != 0u;
+}
+
 // One (token, row slice) work item of the dispatch, done by one wavefront.
 template <int C, bool FP8, bool LL, bool SEND>
 __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int lane) {
@@ -472,11 +491,20 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
         if (cs == kChunkFull || (cs == kChunkPart && g < nchunk)) v[i] = src[g];
     }
 
-    // ---- routing of token t: lane j < k owns slot j
+    // ---- routing of token t: lane j < k owns slot j; with it the layout's
+    // record of the slot (its expert id and in-tile rank)
     int e = -1;
+    uint32_t er = erank_pack(-1, 0);
     if (lane < k) {
         const int64_t v = a.topk_idx[(int64_t)t * k + lane];
+        er = a.erank[(int64_t)t * k + lane];
         if (v >= 0 && v < a.E) e = (int)v;
+    }
+    // a layout made from other routing (topk_idx rewritten in place before a
+    // dispatch that reuses it): the token is dropped and the error recorded
+    if (__ballot(lane < k && (er >> 16) != (erank_pack(e, 0) >> 16)) != 0) {
+        if (s == 0 && lane == 0) atomicOr(a.err, kErrStale);
+        e = -1;
     }
     const int tile = t / kTileTokens;
     const int r = e >= 0 ? e / a.El : 0;
@@ -486,8 +514,8 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
     // of their per-tile counts, or beyond kWalkTiles tiles the layout kernel's
     // prefix over the tiles
     int pre_e = 0, pre_r = 0;
-    if (e >= 0 && tile > 0) {
-        if ((int64_t)a.T <= (int64_t)kWalkTiles * kTileTokens) {
+    if (e >= 0 && tile > 0 && a.mode != kLayoutOneTile) {
+        if (a.mode == kLayoutWalk) {
             pre_e = tile_prefix(a.tile_cnt + (int64_t)e * a.tile_stride, tile);
             if (SEND && first_of_rank) pre_r = tile_prefix(a.tile_cnt + (int64_t)(a.E + r) * a.tile_stride, tile);
         } else {
@@ -498,7 +526,7 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
     int cpos = -1;   // contiguous expert-major row (index into recv_src_idx)
     int rrow = -1;   // receive row (contiguous, or padded low-latency slot)
     if (e >= 0) {
-        const int in_expert = pre_e + a.erank[(int64_t)t * k + lane];   // rank among expert e's rows
+        const int in_expert = pre_e + (int)(er & 0xFFFFu);   // rank among expert e's rows
         cpos = a.eoff[e] + in_expert;
         int64_t row = cpos;
         if (LL) row = (int64_t)e * a.cap + (int64_t)a.s0 * a.max_tokens + in_expert;
@@ -539,6 +567,7 @@ __device__ __forceinline__ void pack_item(const PackArgs& a, int64_t item, int l
         }
     } else {
         // ---- E4M3 quantisation, once per token; 16 lanes hold one 128-channel block
+        if (__ballot(slice_nonfinite<C>(v)) != 0 && lane == 0) atomicOr(a.err, kErrNonFinite);
         u32x2 q[C];
         float sinv[C];
         quantize_slice<C>(v, q, sinv);
@@ -750,6 +779,7 @@ __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
             if (rr >= 0) store_row<C>(reinterpret_cast<u32x4*>(a.recv_rows) + (int64_t)rr * nchunk, v, gbase, lane, nchunk);
         }
     } else {
+        if (__ballot(slice_nonfinite<C>(v)) != 0 && lane == 0) atomicOr(a.err, kErrNonFinite);
         u32x2 q[C];
         float sinv[C];
         quantize_slice<C>(v, q, sinv);
@@ -1051,6 +1081,7 @@ dim3 items_grid(int64_t items, int64_t max_blocks, int waves_per_block = kWavesP
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s) {
+    if (ntiles < 1 || a.mode != layout_mode(ntiles)) return hipErrorInvalidValue;
     if (a.k <= 8) hipLaunchKernelGGL(k_layout<8>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
     else if (a.k <= 16) hipLaunchKernelGGL(k_layout<16>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
     else hipLaunchKernelGGL(k_layout<32>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);

@@ -94,7 +94,7 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     w.off_tile_cnt = take(4 * std::max((size_t)tile_stride(g) * (c->num_experts + c->num_ranks),
                                        (size_t)g.ntiles_max * cnt_stride(c)));
     w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
-    w.off_erank = take(2 * (size_t)c->max_tokens * c->topk);
+    w.off_erank = take(4 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
     w.total = o;
     return w;
@@ -137,6 +137,16 @@ void row_split(int64_t T, int64_t nchunk, int forced, int cap, int* chunks, int*
     *nslices = (int)((nchunk + 64 * c - 1) / (64 * c));
 }
 
+// The status moe_poll_error reports for a set of device error bits.
+moe_status status_of_flags(uint32_t v) {
+    if (v & kErrBadTopk) return MOE_ERR_BAD_TOPK;
+    if (v & kErrStale) return MOE_ERR_STALE_LAYOUT;
+    if (v & kErrCapacity) return MOE_ERR_CAPACITY;
+    if (v & kErrBounds) return MOE_ERR_DEVICE_BOUNDS;
+    if (v & kErrNonFinite) return MOE_ERR_NONFINITE;
+    return MOE_OK;
+}
+
 }  // namespace
 
 struct moe_ctx {
@@ -146,9 +156,10 @@ struct moe_ctx {
     int device;
     char* ws;
     uint32_t tag;
-    // last layout computed into the workspace
+    // last layout computed into the workspace, and the mode it ran in
     const int64_t* layout_idx;
     int32_t layout_T;
+    int32_t layout_mode;
     bool layout_valid;
     // tuning overrides (0 = heuristic)
     int pack_chunks, combine_chunks;
@@ -163,9 +174,6 @@ struct moe_ctx {
     std::vector<int> kid;
 
     uint32_t* err() { return reinterpret_cast<uint32_t*>(ws + wl.off_err); }
-    uint32_t* done() { return reinterpret_cast<uint32_t*>(ws + wl.off_done); }
-    int32_t* i32(size_t off) { return reinterpret_cast<int32_t*>(ws + off); }
-    uint16_t* u16(size_t off) { return reinterpret_cast<uint16_t*>(ws + off); }
 };
 
 namespace {
@@ -182,11 +190,13 @@ const char* kernel_name(int id) {
 }
 
 // Record timing events around one launch when timing is on; log it when asked.
+// ctx may be NULL: then nothing is recorded.
 struct TimedLaunch {
     moe_ctx* ctx;
     hipStream_t s;
     int slot;
     TimedLaunch(moe_ctx* c, hipStream_t st, int id) : ctx(c), s(st), slot(-1) {
+        if (c == nullptr) return;
         if (c->log)
             std::fprintf(stderr, "[moe_ep] ctx %p: %s on stream %p (max_workgroups %d)\n", static_cast<void*>(c),
                          kernel_name(id), static_cast<void*>(st), c->max_blocks);
@@ -201,45 +211,185 @@ struct TimedLaunch {
     }
 };
 
-moe_status run_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t T, int32_t* out_cnt_e,
-                      int32_t* out_cnt_r, uint8_t* out_in_rank, hipStream_t s) {
-    const moe_config& c = ctx->cfg;
+// What the launches of one call need besides their arguments: the
+// configuration, the device workspace, the error word and the launch tuning.
+struct Exec {
+    const moe_config* c;
+    const Geometry* g;
+    const Workspace* wl;
+    char* ws;
+    uint32_t* err;
+    int pack_chunks;
+    int max_blocks;
+    moe_ctx* ctx;   // timing and launch log; NULL for none
+    int32_t* i32(size_t off) const { return reinterpret_cast<int32_t*>(ws + off); }
+    uint16_t* u16(size_t off) const { return reinterpret_cast<uint16_t*>(ws + off); }
+    uint32_t* u32(size_t off) const { return reinterpret_cast<uint32_t*>(ws + off); }
+};
+
+Exec ctx_exec(moe_ctx* ctx) {
+    Exec x;
+    x.c = &ctx->cfg;
+    x.g = &ctx->g;
+    x.wl = &ctx->wl;
+    x.ws = ctx->ws;
+    x.err = ctx->err();
+    x.pack_chunks = ctx->pack_chunks;
+    x.max_blocks = ctx->max_blocks;
+    x.ctx = ctx;
+    return x;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Count + scan launch into the workspace.  *mode receives the layout mode it
+// ran in (the dispatch that consumes this layout is told the same mode).
+moe_status run_layout(const Exec& x, const int64_t* topk_idx, int32_t T, int32_t* out_cnt_e,
+                      int32_t* out_cnt_r, uint8_t* out_in_rank, hipStream_t s, int* mode) {
+    const moe_config& c = *x.c;
+    const int ntiles = std::max(1, (T + kTileTokens - 1) / kTileTokens);
     LayoutArgs a;
     a.topk_idx = topk_idx;
     a.T = T;
     a.k = c.topk;
     a.E = c.num_experts;
     a.R = c.num_ranks;
-    a.El = ctx->g.El;
+    a.El = x.g->El;
     a.k_magic = (uint32_t)(((1u << 20) + c.topk - 1) / c.topk);
-    a.el_magic = (uint32_t)(((1u << 20) + ctx->g.El - 1) / ctx->g.El);
+    a.el_magic = (uint32_t)(((1u << 20) + x.g->El - 1) / x.g->El);
     a.max_tokens = c.max_tokens;
-    a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
-    a.tile_stride = tile_stride(ctx->g);
-    a.cnt_stride = cnt_stride(&ctx->cfg);
-    a.grand_tot = ctx->i32(ctx->wl.off_grand_tot);
-    a.erank = ctx->u16(ctx->wl.off_erank);
-    a.srank = ctx->u16(ctx->wl.off_srank);
-    a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
-    a.cnt_r = ctx->i32(ctx->wl.off_cnt_r);
-    a.eoff = ctx->i32(ctx->wl.off_eoff);
-    a.roff = ctx->i32(ctx->wl.off_roff);
+    a.mode = layout_mode(ntiles);
+    a.in_rank_vec4 = (c.num_ranks % 4 == 0 && aligned4(out_in_rank)) ? 1 : 0;
+    a.tile_cnt = x.i32(x.wl->off_tile_cnt);
+    a.tile_stride = tile_stride(*x.g);
+    a.cnt_stride = cnt_stride(x.c);
+    a.grand_tot = x.i32(x.wl->off_grand_tot);
+    a.erank = x.u32(x.wl->off_erank);
+    a.srank = x.u16(x.wl->off_srank);
+    a.cnt_e = x.i32(x.wl->off_cnt_e);
+    a.cnt_r = x.i32(x.wl->off_cnt_r);
+    a.eoff = x.i32(x.wl->off_eoff);
+    a.roff = x.i32(x.wl->off_roff);
     a.out_cnt_e = out_cnt_e;
     a.out_cnt_r = out_cnt_r;
     a.out_in_rank = out_in_rank;
-    a.err = ctx->err();
-    a.done = ctx->done();
-    const int ntiles = std::max(1, (T + kTileTokens - 1) / kTileTokens);
-    TimedLaunch tl(ctx, s, MOE_KERNEL_LAYOUT);
+    a.err = x.err;
+    a.done = x.u32(x.wl->off_done);
+    TimedLaunch tl(x.ctx, s, MOE_KERNEL_LAYOUT);
     hipError_t e = launch_layout(a, ntiles, s);
     tl.done();
-    if (e != hipSuccess) {
-        ctx->layout_valid = false;
-        return MOE_ERR_HIP;
+    *mode = a.mode;
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status check_dispatch_args(const moe_config& c, const void* x, const int64_t* topk_idx, int32_t num_tokens,
+                               const moe_dispatch_buffers* bufs, const moe_handle* handle) {
+    const bool fp8 = c.quant == MOE_QUANT_FP8_E4M3;
+    const bool ll = c.layout == MOE_LAYOUT_PADDED_LL;
+    if (bufs == nullptr || handle == nullptr) return MOE_ERR_INVALID_ARG;
+    if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens > 0 && (x == nullptr || topk_idx == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (bufs->recv_rows == nullptr || !aligned16(x) || !aligned16(bufs->recv_rows)) return MOE_ERR_INVALID_ARG;
+    if (ll) {
+        if (bufs->send_rows != nullptr || bufs->send_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (bufs->send_rows == nullptr || !aligned16(bufs->send_rows)) return MOE_ERR_INVALID_ARG;
+        if (fp8 != (bufs->send_scales != nullptr)) return MOE_ERR_INVALID_ARG;
     }
-    ctx->layout_idx = topk_idx;
-    ctx->layout_T = T;
-    ctx->layout_valid = true;
+    if (fp8 != (bufs->recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (handle->pos == nullptr || handle->expert_offsets == nullptr || handle->rank_offsets == nullptr ||
+        handle->send_src_idx == nullptr || handle->recv_src_idx == nullptr || handle->recv_counts == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// The dispatch proper (arguments already checked).  reuse_mode >= 0: reuse
+// the layout already in the workspace, computed in that mode; -1: compute it
+// here first (or, for decode-sized padded batches, run the fused launch,
+// which leaves the workspace alone).  *new_layout_mode receives the mode of a
+// layout computed here, else -1.
+moe_status run_dispatch(const Exec& xc, const void* x, const int64_t* topk_idx, int32_t num_tokens,
+                        int reuse_mode, const moe_dispatch_buffers* bufs, moe_handle* handle, uint32_t tag,
+                        hipStream_t s, int* new_layout_mode) {
+    *new_layout_mode = -1;
+    const moe_config& c = *xc.c;
+    const bool fp8 = c.quant == MOE_QUANT_FP8_E4M3;
+    const bool ll = c.layout == MOE_LAYOUT_PADDED_LL;
+    // low latency without a reused layout: one fused launch when the routing is small
+    const bool fused = reuse_mode < 0 && ll && (int64_t)num_tokens * c.topk <= kFusedMaxEntries &&
+                       num_tokens <= kFusedMaxTokens;
+    int mode = reuse_mode;
+    if (reuse_mode < 0 && !fused) {
+        moe_status st = run_layout(xc, topk_idx, num_tokens, nullptr, nullptr, nullptr, s, &mode);
+        if (st != MOE_OK) return st;
+        *new_layout_mode = mode;
+    }
+
+    PackArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.topk_idx = topk_idx;
+    a.T = num_tokens;
+    a.k = c.topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.El = xc.g->El;
+    a.H = c.hidden;
+    a.rbits = xc.g->rbits;
+    a.max_tokens = c.max_tokens;
+    a.s0 = c.src_rank;
+    a.cap = xc.g->cap;
+    a.tile_cnt = xc.i32(xc.wl->off_tile_cnt);
+    a.tile_stride = tile_stride(*xc.g);
+    a.cnt_stride = cnt_stride(xc.c);
+    a.mode = mode;
+    a.erank = xc.u32(xc.wl->off_erank);
+    a.srank = xc.u16(xc.wl->off_srank);
+    a.cnt_e = xc.i32(xc.wl->off_cnt_e);
+    a.eoff = xc.i32(xc.wl->off_eoff);
+    a.roff = xc.i32(xc.wl->off_roff);
+    a.send_rows = bufs->send_rows;
+    a.send_scales = bufs->send_scales;
+    a.recv_rows = bufs->recv_rows;
+    a.recv_scales = bufs->recv_scales;
+    a.send_cap_rows = xc.g->send_rows;
+    a.recv_cap_rows = xc.g->recv_rows;
+    a.pairs_cap = (int64_t)c.max_tokens * c.topk;
+    a.h_pos = handle->pos;
+    a.h_eoff = handle->expert_offsets;
+    a.h_roff = handle->rank_offsets;
+    a.h_send_src = handle->send_src_idx;
+    a.h_recv_src = handle->recv_src_idx;
+    a.h_recv_counts = handle->recv_counts;
+    a.err = xc.err;
+    int chunks, nslices;
+    row_split(num_tokens, c.hidden / 8, xc.pack_chunks, 1, &chunks, &nslices);
+    a.nslices = nslices;
+    a.ll_bpt = 1;
+    TimedLaunch tl(xc.ctx, s, MOE_KERNEL_DISPATCH);
+    hipError_t e;
+    if (fused) {
+        // ll_bpt blocks per token whose wavefronts each copy one 64-chunk slice:
+        // 512-thread blocks when the row has more than 256 chunks (the
+        // workspace is neither read nor written here)
+        const int64_t nchunk = c.hidden / 8;
+        const int nt = nchunk > kBlockThreads ? 512 : kBlockThreads;
+        a.nslices = (int)((nchunk + 63) / 64);
+        a.ll_bpt = (a.nslices + nt / 64 - 1) / (nt / 64);
+        e = launch_ll_fused(a, 1, nt, fp8, s);
+    } else if (num_tokens == 0) {
+        // grid of one block: block 0 copies the offsets, every wave exits (no
+        // items); at least one block so that the handle's offsets and counts
+        // are written for T = 0
+        a.nslices = 1;
+        e = launch_pack(a, 1, fp8, ll, !ll, xc.max_blocks, s);
+    } else {
+        e = launch_pack(a, chunks, fp8, ll, !ll, xc.max_blocks, s);
+    }
+    tl.done();
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    handle->num_tokens = num_tokens;
+    handle->tag = tag;
     return MOE_OK;
 }
 
@@ -256,6 +406,8 @@ MOE_API const char* moe_status_str(moe_status s) {
         case MOE_ERR_HIP: return "MOE_ERR_HIP";
         case MOE_ERR_BAD_TOPK: return "MOE_ERR_BAD_TOPK";
         case MOE_ERR_DEVICE_BOUNDS: return "MOE_ERR_DEVICE_BOUNDS";
+        case MOE_ERR_STALE_LAYOUT: return "MOE_ERR_STALE_LAYOUT";
+        case MOE_ERR_NONFINITE: return "MOE_ERR_NONFINITE";
     }
     return "MOE_ERR_UNKNOWN";
 }
@@ -310,6 +462,7 @@ MOE_API moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out) {
     ctx->tag = config_tag(cfg);
     ctx->layout_idx = nullptr;
     ctx->layout_T = -1;
+    ctx->layout_mode = -1;
     ctx->layout_valid = false;
     ctx->pack_chunks = 0;
     ctx->combine_chunks = 0;
@@ -415,109 +568,36 @@ MOE_API moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, in
     if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
     if (num_tokens > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
     if (num_tokens > 0 && topk_idx == nullptr) return MOE_ERR_INVALID_ARG;
-    return run_layout(ctx, topk_idx, num_tokens, num_tokens_per_expert, num_tokens_per_rank,
-                      is_token_in_rank, reinterpret_cast<hipStream_t>(stream));
+    int mode = -1;
+    const moe_status st = run_layout(ctx_exec(ctx), topk_idx, num_tokens, num_tokens_per_expert,
+                                     num_tokens_per_rank, is_token_in_rank, reinterpret_cast<hipStream_t>(stream),
+                                     &mode);
+    ctx->layout_valid = st == MOE_OK;
+    ctx->layout_idx = topk_idx;
+    ctx->layout_T = num_tokens;
+    ctx->layout_mode = mode;
+    return st;
 }
 
 MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, int32_t num_tokens,
                                 int32_t reuse_layout, const moe_dispatch_buffers* bufs, moe_handle* handle,
                                 void* stream) {
-    if (ctx == nullptr || bufs == nullptr || handle == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    const bool fp8 = c.quant == MOE_QUANT_FP8_E4M3;
-    const bool ll = c.layout == MOE_LAYOUT_PADDED_LL;
-    if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
-    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
-    if (num_tokens > 0 && (x == nullptr || topk_idx == nullptr)) return MOE_ERR_INVALID_ARG;
-    if (bufs->recv_rows == nullptr || !aligned16(x) || !aligned16(bufs->recv_rows)) return MOE_ERR_INVALID_ARG;
-    if (ll) {
-        if (bufs->send_rows != nullptr || bufs->send_scales != nullptr) return MOE_ERR_INVALID_ARG;
-    } else {
-        if (bufs->send_rows == nullptr || !aligned16(bufs->send_rows)) return MOE_ERR_INVALID_ARG;
-        if (fp8 != (bufs->send_scales != nullptr)) return MOE_ERR_INVALID_ARG;
-    }
-    if (fp8 != (bufs->recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
-    if (handle->pos == nullptr || handle->expert_offsets == nullptr || handle->rank_offsets == nullptr ||
-        handle->send_src_idx == nullptr || handle->recv_src_idx == nullptr || handle->recv_counts == nullptr)
-        return MOE_ERR_INVALID_ARG;
+    if (ctx == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
+    const moe_status st = check_dispatch_args(ctx->cfg, x, topk_idx, num_tokens, bufs, handle);
+    if (st != MOE_OK) return st;
     if (reuse_layout != 0 && reuse_layout != 1) return MOE_ERR_INVALID_ARG;
     if (reuse_layout && (!ctx->layout_valid || ctx->layout_idx != topk_idx || ctx->layout_T != num_tokens))
         return MOE_ERR_INVALID_ARG;
-
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // low latency without a reused layout: one fused launch when the routing is small
-    const bool fused = !reuse_layout && ll && (int64_t)num_tokens * c.topk <= kFusedMaxEntries &&
-                       num_tokens <= kFusedMaxTokens;
-    if (!reuse_layout && !fused) {
-        moe_status st = run_layout(ctx, topk_idx, num_tokens, nullptr, nullptr, nullptr, s);
-        if (st != MOE_OK) return st;
+    int computed = -1;
+    const moe_status rs = run_dispatch(ctx_exec(ctx), x, topk_idx, num_tokens, reuse_layout ? ctx->layout_mode : -1,
+                                       bufs, handle, ctx->tag, reinterpret_cast<hipStream_t>(stream), &computed);
+    if (computed >= 0) {   // a layout computed inside this call is now the context's last one
+        ctx->layout_valid = true;
+        ctx->layout_idx = topk_idx;
+        ctx->layout_T = num_tokens;
+        ctx->layout_mode = computed;
     }
-
-    PackArgs a;
-    a.x = static_cast<const uint16_t*>(x);
-    a.topk_idx = topk_idx;
-    a.T = num_tokens;
-    a.k = c.topk;
-    a.E = c.num_experts;
-    a.R = c.num_ranks;
-    a.El = ctx->g.El;
-    a.H = c.hidden;
-    a.rbits = ctx->g.rbits;
-    a.max_tokens = c.max_tokens;
-    a.s0 = c.src_rank;
-    a.cap = ctx->g.cap;
-    a.tile_cnt = ctx->i32(ctx->wl.off_tile_cnt);
-    a.tile_stride = tile_stride(ctx->g);
-    a.cnt_stride = cnt_stride(&ctx->cfg);
-    a.erank = ctx->u16(ctx->wl.off_erank);
-    a.srank = ctx->u16(ctx->wl.off_srank);
-    a.cnt_e = ctx->i32(ctx->wl.off_cnt_e);
-    a.eoff = ctx->i32(ctx->wl.off_eoff);
-    a.roff = ctx->i32(ctx->wl.off_roff);
-    a.send_rows = bufs->send_rows;
-    a.send_scales = bufs->send_scales;
-    a.recv_rows = bufs->recv_rows;
-    a.recv_scales = bufs->recv_scales;
-    a.send_cap_rows = ctx->g.send_rows;
-    a.recv_cap_rows = ctx->g.recv_rows;
-    a.pairs_cap = (int64_t)c.max_tokens * c.topk;
-    a.h_pos = handle->pos;
-    a.h_eoff = handle->expert_offsets;
-    a.h_roff = handle->rank_offsets;
-    a.h_send_src = handle->send_src_idx;
-    a.h_recv_src = handle->recv_src_idx;
-    a.h_recv_counts = handle->recv_counts;
-    a.err = ctx->err();
-    int chunks, nslices;
-    row_split(num_tokens, c.hidden / 8, ctx->pack_chunks, 1, &chunks, &nslices);
-    a.nslices = nslices;
-    a.ll_bpt = 1;
-    // at least one block so that the handle's offsets and counts are written for T = 0
-    PackArgs a0 = a;
-    if (num_tokens == 0) a0.T = 0;
-    TimedLaunch tl(ctx, s, MOE_KERNEL_DISPATCH);
-    hipError_t e;
-    if (fused) {
-        // ll_bpt blocks per token whose wavefronts each copy one 64-chunk slice:
-        // 512-thread blocks when the row has more than 256 chunks (the
-        // context's layout state is neither read nor written here)
-        const int64_t nchunk = c.hidden / 8;
-        const int nt = nchunk > kBlockThreads ? 512 : kBlockThreads;
-        a.nslices = (int)((nchunk + 63) / 64);
-        a.ll_bpt = (a.nslices + nt / 64 - 1) / (nt / 64);
-        e = launch_ll_fused(a, 1, nt, fp8, s);
-    } else if (num_tokens == 0) {
-        // grid of one block: block 0 copies the offsets, every wave exits (no items)
-        a0.nslices = 1;
-        e = launch_pack(a0, 1, fp8, ll, !ll, ctx->max_blocks, s);
-    } else {
-        e = launch_pack(a, chunks, fp8, ll, !ll, ctx->max_blocks, s);
-    }
-    tl.done();
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    handle->num_tokens = num_tokens;
-    handle->tag = ctx->tag;
-    return MOE_OK;
+    return rs;
 }
 
 MOE_API moe_status moe_combine(moe_ctx* ctx, const void* expert_out, const float* topk_weights,
@@ -638,10 +718,7 @@ MOE_API moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags) {
     if (v != 0 && hipMemset(ctx->err(), 0, 4) != hipSuccess) return MOE_ERR_HIP;
     if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
     if (flags) *flags = v;
-    if (v & kErrBadTopk) return MOE_ERR_BAD_TOPK;
-    if (v & kErrCapacity) return MOE_ERR_CAPACITY;
-    if (v & kErrBounds) return MOE_ERR_DEVICE_BOUNDS;
-    return MOE_OK;
+    return status_of_flags(v);
 }
 
 MOE_API moe_status moe_timing_begin(moe_ctx* ctx, int32_t max_launches) {
@@ -716,3 +793,4 @@ MOE_API moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launc
     }
     return st;
 }
+

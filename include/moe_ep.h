@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 3   /* 3: moe_timing_launches */
+#define MOE_EP_ABI_VERSION 4   /* 3: moe_timing_launches; 4: stale-layout and non-finite
+                                  flags */
 
 /* ---------------------------------------------------------------- status */
 typedef enum moe_status {
@@ -66,9 +67,15 @@ typedef enum moe_status {
     MOE_ERR_HANDLE = 4,        /* handle not produced by moe_dispatch on a compatible context */
     MOE_ERR_HIP = 5,           /* a HIP runtime call failed */
     MOE_ERR_BAD_TOPK = 6,      /* from moe_poll_error: an expert id outside [-1, E) was seen */
-    MOE_ERR_DEVICE_BOUNDS = 7  /* from moe_poll_error: a computed row fell outside its buffer
-                                  (topk_idx changed between moe_dispatch_layout and a
-                                  moe_dispatch that reused its layout); the row was dropped */
+    MOE_ERR_DEVICE_BOUNDS = 7, /* from moe_poll_error: a computed row fell outside its buffer;
+                                  the row was dropped */
+    MOE_ERR_STALE_LAYOUT = 8,  /* from moe_poll_error: a moe_dispatch with reuse_layout = 1 found
+                                  topk_idx entries that differ from the ones its layout was
+                                  computed from (rewritten in place in between); every such
+                                  token was dropped (pos -1, no rows written) */
+    MOE_ERR_NONFINITE = 9      /* from moe_poll_error: an fp8 dispatch met Inf or NaN in a
+                                  128-channel block of x; that block's codes and scale are
+                                  unspecified (every other block is exact) */
 } moe_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -131,9 +138,13 @@ typedef enum moe_buffer_kind {
     MOE_BUF_KIND_COUNT = 16
 } moe_buffer_kind;
 
-/* Bytes needed for one buffer kind under `cfg` (host pointers).  Pure host
- * computation; needs no GPU.  Returns MOE_ERR_INVALID_ARG / UNSUPPORTED for a
- * bad config or kind. */
+/* Bytes needed for one buffer kind under `cfg` (host pointers): the pages'
+ * size-hint call for preallocated, fixed-size buffers (guide, "Low-latency
+ * mode key features": a size hint and pre-allocation; "Performance tuning":
+ * buffers made once with low_latency_mode=True, fixed-size buffers instead of
+ * queues).  Every size is a static upper bound for num_tokens <= max_tokens.
+ * Pure host computation; needs no GPU.  Returns MOE_ERR_INVALID_ARG /
+ * UNSUPPORTED for a bad config or kind. */
 moe_status moe_size_hint(const moe_config* cfg, int32_t kind, size_t* bytes);
 
 /* ---------------------------------------------------------------- context */
@@ -141,7 +152,11 @@ typedef struct moe_ctx moe_ctx;
 
 /* Validate `cfg` (host) and allocate the context and its device workspace
  * (per-tile histograms and scan state, within-tile ranks, error word) on the
- * current HIP device.  The only call that allocates.  On error *out is NULL. */
+ * current HIP device: the pages' preallocated Buffer (guide, "Low-latency mode
+ * key features": pre-allocation to avoid run-time allocation; "Performance
+ * tuning": the buffer is created once, in low-latency mode with
+ * low_latency_mode=True).  The only call that allocates.  On error *out is
+ * NULL. */
 moe_status moe_ctx_create(const moe_config* cfg, moe_ctx** out);
 
 /* Free the context.  Synchronizes the device first.  NULL is a no-op. */
@@ -166,6 +181,8 @@ moe_status moe_ctx_tune(moe_ctx* ctx, int32_t dispatch_chunks, int32_t combine_c
  *   num_tokens_per_expert  int32 [E]:  valid slots routed to expert e
  *   num_tokens_per_rank    int32 [R]:  tokens with at least one expert on rank r
  *   is_token_in_rank       uint8 [num_tokens, R]: 1 iff token t goes to rank r
+ *                          (any alignment; 32-bit stores when it is 4-byte
+ *                          aligned and R % 4 == 0, byte stores otherwise)
  * Any output pointer may be NULL (not written).  0 <= num_tokens <= max_tokens.
  * Also keeps, in the context's workspace, the scan state a following
  * moe_dispatch(..., reuse_layout = 1) consumes. */
@@ -194,7 +211,13 @@ typedef struct moe_dispatch_buffers {
 } moe_dispatch_buffers;
 
 /* Routing record written by moe_dispatch and read by moe_combine (host struct
- * of caller-owned device buffers, sized by the MOE_BUF_HANDLE_* hints).
+ * of caller-owned device buffers, sized by the MOE_BUF_HANDLE_* hints).  The
+ * pages' handle is returned by dispatch and passed to combine (guide, "Core
+ * API example").  Here the caller owns the storage and the handle carries a
+ * tag of the configuration that produced it, instead of a generation counter
+ * held by the library: a handle stays valid until the caller reuses its
+ * arrays, and moe_combine rejects one from an incompatible configuration
+ * (MOE_ERR_HANDLE) rather than reporting a stale generation.
  *   pos[t, j]        row of slot j of token t in the receive layout
  *                    (CONTIGUOUS: expert-major row; PADDED_LL: e*cap + slot),
  *                    -1 for an empty slot or a row that was not placed
@@ -225,14 +248,22 @@ typedef struct moe_handle {
  *                    MOE_LAYOUT_PADDED_LL with num_tokens * topk <= 2048 and
  *                    num_tokens <= 512 the
  *                    routing and the copy run as one fused launch instead);
- *                 1: reuse the scan state of the last moe_dispatch_layout on this
- *                    context, which must have seen the same topk_idx pointer and
- *                    num_tokens (checked; the contents must not have changed)
+ *                 1: reuse the scan state of the last layout computed on this
+ *                    context (by moe_dispatch_layout, or inside a moe_dispatch
+ *                    with reuse_layout = 0), which must have seen the same
+ *                    topk_idx pointer and num_tokens (checked on the host).
+ *                    The contents must not have changed either: the kernel
+ *                    compares every entry with the expert id the layout
+ *                    recorded, drops each token with a changed entry and sets
+ *                    MOE_ERR_STALE_LAYOUT (moe_poll_error)
  *   bufs       output rows (and scales for fp8)
  *   handle     host struct; its device arrays are written, num_tokens/tag set
  * fp8 rows: per token and 128-channel block, a = max|x|, a' = max(a, 1e-4),
  * codes = E4M3(x * (448/a')) with round-to-nearest-even (saturating), stored
- * scale = a'/448.  Every destination gets the same bytes. */
+ * scale = a'/448.  Every destination gets the same bytes.  The rows must be
+ * finite: for a block holding Inf or NaN the codes and scale are unspecified
+ * and moe_poll_error reports MOE_ERR_NONFINITE (bf16 rows are copied bit for
+ * bit whatever they hold). */
 moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, int32_t num_tokens,
                         int32_t reuse_layout, const moe_dispatch_buffers* bufs,
                         moe_handle* handle, void* stream);
@@ -317,10 +348,11 @@ moe_status moe_hook_wait(const moe_hook* hook, void* stream);
 
 /* ---------------------------------------------------------------- errors */
 /* Synchronize `stream`, read and clear the sticky device error word.
- * Returns MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY or MOE_ERR_DEVICE_BOUNDS
- * (the first set, in that order); *flags (host, may be NULL) receives the raw
- * bits (1: bad expert id, 2: row outside its buffer, 4: low-latency window
- * overflow). */
+ * Returns MOE_OK, MOE_ERR_BAD_TOPK, MOE_ERR_STALE_LAYOUT, MOE_ERR_CAPACITY,
+ * MOE_ERR_DEVICE_BOUNDS or MOE_ERR_NONFINITE (the first set, in that order);
+ * *flags (host, may be NULL) receives the raw bits (1: bad expert id, 2: row
+ * outside its buffer, 4: low-latency window overflow, 8: stale reused layout,
+ * 16: non-finite fp8 input). */
 moe_status moe_poll_error(moe_ctx* ctx, void* stream, uint32_t* flags);
 
 /* ---------------------------------------------------------------- timing */

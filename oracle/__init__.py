@@ -150,19 +150,11 @@ def quant_rows(x_bf16):
     return q, s
 
 
-def dispatch(x_bf16, topk_idx, num_experts, num_ranks, quant=0, max_tokens=0,
-             src_rank=0, with_send=True):
-    """Layout + positions + payload rows.
-
-    Returns a dict with every layout/handle array, the packed send rows
-    (rank-major, N_send rows) and the expert-major receive rows (N_pairs rows,
-    row i = token recv_src_idx[i]).  For the low-latency padded layout the
-    receive rows are the same; their padded addresses are pos_ll.
-    """
+def rows(x_bf16, pp, quant=0, with_send=True):
+    """Step 3 (payload): the packed send rows and the expert-major receive rows
+    of `pp` (the result of positions()), bf16 copies or E4M3 codes + scales."""
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
-    lay = layout(topk_idx, num_experts, num_ranks)
-    pp = positions(topk_idx, num_experts, num_ranks, lay, max_tokens, src_rank)
     n_send, n_pairs = pp["n_send"], pp["n_pairs"]
     if quant == 0:
         send = np.empty((n_send, H), np.uint16) if with_send else None
@@ -176,10 +168,23 @@ def dispatch(x_bf16, topk_idx, num_experts, num_ranks, quant=0, max_tokens=0,
     _load().orc_dispatch_rows(_p(x), H, quant, _p(pp["send_src_idx"]), n_send,
                               _p(pp["recv_src_idx"]), n_pairs, _p(send), _p(send_s),
                               _p(recv), _p(recv_s))
+    return {"send_rows": send, "send_scales": send_s, "recv_rows": recv, "recv_scales": recv_s}
+
+
+def dispatch(x_bf16, topk_idx, num_experts, num_ranks, quant=0, max_tokens=0,
+             src_rank=0, with_send=True):
+    """Layout + positions + payload rows.
+
+    Returns a dict with every layout/handle array, the packed send rows
+    (rank-major, N_send rows) and the expert-major receive rows (N_pairs rows,
+    row i = token recv_src_idx[i]).  For the low-latency padded layout the
+    receive rows are the same; their padded addresses are pos_ll.
+    """
+    lay = layout(topk_idx, num_experts, num_ranks)
+    pp = positions(topk_idx, num_experts, num_ranks, lay, max_tokens, src_rank)
     out = dict(lay)
     out.update(pp)
-    out.update({"send_rows": send, "send_scales": send_s,
-                "recv_rows": recv, "recv_scales": recv_s})
+    out.update(rows(x_bf16, pp, quant, with_send))
     return out
 
 

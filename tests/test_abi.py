@@ -43,7 +43,8 @@ def test_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARG"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_CAPACITY"), (4, "MOE_ERR_HANDLE"), (5, "MOE_ERR_HIP"),
-                       (6, "MOE_ERR_BAD_TOPK"), (7, "MOE_ERR_DEVICE_BOUNDS")]:
+                       (6, "MOE_ERR_BAD_TOPK"), (7, "MOE_ERR_DEVICE_BOUNDS"), (8, "MOE_ERR_STALE_LAYOUT"),
+                       (9, "MOE_ERR_NONFINITE")]:
         assert moe.status_str(code) == name
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
 

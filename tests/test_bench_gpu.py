@@ -37,8 +37,13 @@ def check_line(d, steps, warmup):
         assert key in rf, key
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    # the headline is the cold protocol; warm is reported beside it
+    assert rf["frac_cold"] == rf["frac"] and rf["frac_warm"] > 0
+    assert "cold" in d["protocol"] and d["warm"]["ms_per_step"] > 0
+    assert len(d["us_per_step_p10_p50_p90"]) == 3
     for k in d["kernels"].values():
-        assert k["us"] > 0 and len(k["us_p10_p50_p90"]) == 3
+        assert k["us"] == k["us_cold"] > 0 and len(k["us_cold_p10_p50_p90"]) == 3
+        assert k["us_warm"] > 0 and len(k["us_warm_p10_p50_p90"]) == 3
 
 
 def test_bench_line_prefill():

@@ -82,20 +82,61 @@ def test_kernel_table_reports_percentiles_and_cold_passes():
     assert t["dispatch"]["us_cold_p10_p50_p90"] == [200.0, 200.0, 200.0]
 
 
-def test_cpu_baseline_runs_whole_steps_for_the_time_asked():
-    """The oracle baseline repeats whole steps until the CPU time asked for is
-    spent (at least three), and reports the median step."""
+def test_kernel_passes_reports_every_pass_and_the_primary():
+    mk = lambda ms: {"total_ms": sum(ms), "launches": len(ms), "ms": ms}
+    none = {"total_ms": 0.0, "launches": 0, "ms": []}
+    passes = {"cold": {"dispatch": mk([0.2, 0.2, 0.2]), "combine": none},
+              "warm": {"dispatch": mk([0.1, 0.1, 0.1]), "combine": none}}
+    t = bench.kernel_passes(passes, {"dispatch": 1_000_000, "combine": 5}, "cold")
+    assert set(t) == {"dispatch"}                       # kernels with no launch are left out
+    k = t["dispatch"]
+    assert k["us"] == k["us_cold"] == 200.0 and k["GB/s"] == k["GB/s_cold"] == 5.0
+    assert k["us_warm"] == 100.0 and k["GB/s_warm"] == 10.0 and k["GB/s_cold_p50"] == 5.0
+    assert k["us_cold_p10_p50_p90"] == [200.0, 200.0, 200.0]
+
+
+def _tiny_state():
     import torch
     d = W.make("tiny")
     c = d["cfg"]
     ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
     n = ref["n_pairs"]
     y = torch.from_numpy(W.expert_outputs(d, n).view(np.int16)).view(torch.bfloat16)
-    s = {"d": d, "c": c, "y": y, "n_pairs": n}
-    med, runs, total = bench.cpu_baseline(s, 0.0)
-    assert runs == 3 and med > 0 and total >= med
-    med, runs, total = bench.cpu_baseline(s, 0.2)
-    assert total >= 0.2 and runs > 3 and med <= total
+    return d, c, y, ref
+
+
+def test_oracle_timing_runs_for_the_time_asked_and_splits_the_ops():
+    """The oracle baseline repeats steps until the CPU time asked for is spent
+    (at least three), timing layout, dispatch and combine each on its own, and
+    reports their medians; pinned to one core and unpinned afterwards."""
+    d, c, y, _ = _tiny_state()
+    s = {"d": d, "c": c, "y": y}
+    before = os.sched_getaffinity(0)
+    o = bench.oracle_timing(s, seconds=0.0)
+    assert o["runs"] == 3 and os.sched_getaffinity(0) == before
+    for key in ("layout_ms", "dispatch_ms", "combine_ms", "step_ms"):
+        assert o[key] > 0, key
+    o = bench.oracle_timing(s, seconds=0.2)
+    assert o["cpu_seconds"] >= 0.2 and o["runs"] > 3
+    o = bench.oracle_timing(s, runs=7)
+    assert o["runs"] == 7
+
+
+def test_oracle_ops_are_the_oracle_step():
+    """The three timed ops together compute what oracle.dispatch + combine
+    compute (the timing splits the step, it does not change it)."""
+    d, c, y, ref = _tiny_state()
+    s = {"d": d, "c": c, "y": y}
+    yb, kw = bench.oracle_inputs(s)
+    combined = []
+    real_combine = oracle.combine
+    try:
+        oracle.combine = lambda yy, w, pos: combined.append(real_combine(yy, w, pos))
+        bench.oracle_ops(s, yb, kw)
+    finally:
+        oracle.combine = real_combine
+    expect = real_combine(y.view(__import__("torch").int16).numpy().view(np.uint16), d["topk_weights"], ref["pos"])
+    assert len(combined) == 1 and np.array_equal(combined[0], expect)
 
 
 def test_host_time_per_call_is_the_median_call():
@@ -115,21 +156,14 @@ def test_host_time_per_call_is_the_median_call():
     assert 0 < us < 1000                       # the median ignores the 2 ms outliers
 
 
-def test_oracle_step_per_workload_in_both_receive_modes(monkeypatch):
-    """The per-workload oracle time runs whole oracle steps (the requested
-    number, pinned to one core and then unpinned), in the contiguous mode and in
-    the padded low-latency mode; in the padded mode the combine reads the
-    expert outputs at the oracle's own padded rows."""
+def test_oracle_inputs_in_both_receive_modes():
+    """In the padded low-latency mode the oracle's combine reads the expert
+    outputs at the oracle's own padded rows, gathered into its expert-major
+    order: the same values as in the contiguous mode."""
     import torch
-    d = W.make("tiny")
-    c = d["cfg"]
-    ref = oracle.dispatch(d["x"], d["topk_idx"], c["E"], c["R"], quant=c["quant"])
-    n = ref["n_pairs"]
-    y = torch.from_numpy(W.expert_outputs(d, n).view(np.int16)).view(torch.bfloat16)
-    before = os.sched_getaffinity(0)
-    assert bench.oracle_step_ms({"d": d, "c": c, "y": y}, 3) > 0
-    assert os.sched_getaffinity(0) == before
-
+    d, c, y, ref = _tiny_state()
+    y_c, kw = bench.oracle_inputs({"d": d, "c": c, "y": y})
+    assert kw["with_send"] and kw["max_tokens"] == 0
     # the same tokens in the padded layout: expert outputs at e * cap + slot
     cl = dict(c, layout=1, max_tokens=c["T"])
     cap = cl["max_tokens"] * c["R"]
@@ -139,10 +173,8 @@ def test_oracle_step_per_workload_in_both_receive_modes(monkeypatch):
     y_pad = torch.zeros((c["E"] * cap, c["H"]), dtype=torch.bfloat16)
     y_pad[torch.from_numpy(ll["pos_ll"][valid].astype(np.int64))] = y[torch.from_numpy(
         ll["pos"][valid].astype(np.int64))]
-    combined = []
-    real_combine = oracle.combine
-    monkeypatch.setattr(oracle, "combine", lambda yy, w, pos: combined.append(real_combine(yy, w, pos)))
-    assert bench.oracle_step_ms({"d": d, "c": cl, "y": y_pad}, 2) > 0
-    assert len(combined) == 2
-    expect = real_combine(y.view(torch.int16).numpy().view(np.uint16), d["topk_weights"], ref["pos"])
-    assert all(np.array_equal(o, expect) for o in combined)
+    y_l, kw_l = bench.oracle_inputs({"d": d, "c": cl, "y": y_pad})
+    assert not kw_l["with_send"] and kw_l["max_tokens"] == c["T"]
+    assert np.array_equal(y_l, y_c)
+    o = bench.oracle_timing({"d": d, "c": cl, "y": y_pad}, runs=2)
+    assert o["runs"] == 2 and o["combine_ms"] > 0
