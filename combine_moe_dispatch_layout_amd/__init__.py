@@ -13,9 +13,9 @@ from ._binding import (  # noqa: F401
     MOE_BUF_SEND_SCALES, MOE_BUF_WORKSPACE, MOE_ERR_BAD_TOPK, MOE_ERR_CAPACITY,
     MOE_ERR_DEVICE_BOUNDS, MOE_ERR_HANDLE, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_NONFINITE,
     MOE_ERR_STALE_LAYOUT, MOE_ERR_UNSUPPORTED, ERR_FLAG_BAD_TOPK, ERR_FLAG_BOUNDS, ERR_FLAG_CAPACITY,
-    ERR_FLAG_NONFINITE, ERR_FLAG_STALE,
+    ERR_FLAG_NONFINITE, ERR_FLAG_STALE, StaticConfig,
     MOE_KERNEL_COMBINE, MOE_KERNEL_COMBINE_BWD, MOE_KERNEL_DISPATCH, MOE_KERNEL_DISPATCH_BWD,
     MOE_KERNEL_LAYOUT, MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_PADDED_LL, MOE_OK, MOE_QUANT_BF16,
     MOE_QUANT_FP8_E4M3, load_library, make_config, moe_combine, moe_combine_backward, moe_dispatch,
-    moe_dispatch_backward, moe_dispatch_layout, moe_poll_error, moe_size_hint, prepare_combine,
+    moe_dispatch_backward, moe_dispatch_layout, moe_dispatch_noalloc, moe_poll_error, moe_size_hint, prepare_combine,
     prepare_dispatch, status_str)

@@ -76,7 +76,7 @@ EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy
            "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_backward",
            "moe_combine_backward", "moe_ctx_set_max_workgroups", "moe_hook_create", "moe_hook_destroy",
            "moe_hook_record", "moe_hook_wait", "moe_poll_error", "moe_timing_begin", "moe_timing_end",
-           "moe_timing_launches")
+           "moe_timing_launches", "moe_dispatch_noalloc")
 
 _lib = None
 
@@ -115,6 +115,8 @@ def load_library(path=LIB_PATH):
         "moe_timing_end": [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
         "moe_timing_launches": [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float), i32,
                                 ctypes.POINTER(ctypes.c_int32)],
+        "moe_dispatch_noalloc": [ctypes.POINTER(moe_config), vp, vp, i32, ctypes.POINTER(moe_dispatch_buffers),
+                                 ctypes.POINTER(moe_handle), vp, vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -523,6 +525,45 @@ def prepare_combine(ctx, expert_out, topk_weights, handle, out, num_tokens, stre
         if st != MOE_OK:
             raise MoeError(st, "moe_combine")
     return call
+
+
+class StaticConfig:
+    """A configuration without a context (for moe_dispatch_noalloc): sizes
+    for Handle and DispatchBuffers on the current device, nothing allocated by
+    the library."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        self.device = torch.cuda.current_device()
+        self._fit_token = object()
+
+    def hint(self, kind):
+        cache = self.__dict__.setdefault("_hints", {})
+        if kind not in cache:
+            cache[kind] = moe_size_hint(self.cfg, kind)
+        return cache[kind]
+
+
+def moe_dispatch_noalloc(scfg, x, topk_idx, bufs, handle, error_word=None):
+    """moe_dispatch without a context or any allocation: the library's static
+    per-GPU scratch holds the layout.  scfg: a StaticConfig (or a Context, for
+    its configuration); bufs and handle sized for it.  error_word: optional
+    int32/uint32 device tensor of one element that collects moe_poll_error's
+    bits.  Returns (bufs, handle)."""
+    c = scfg.cfg
+    _as_dev(x, torch.bfloat16, "x")
+    _as_dev(topk_idx, torch.int64, "topk_idx")
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != c.hidden or tuple(topk_idx.shape) != (T, c.topk):
+        raise ValueError("x must be [T, %d] and topk_idx [T, %d]" % (c.hidden, c.topk))
+    _check_bufs(scfg, bufs)
+    _check_handle(scfg, handle)
+    if error_word is not None and not (error_word.is_cuda and error_word.element_size() == 4):
+        raise TypeError("error_word must be a 4-byte CUDA tensor")
+    _check(load_library().moe_dispatch_noalloc(ctypes.byref(c), _ptr(x), _ptr(topk_idx), T, ctypes.byref(bufs.c),
+                                               ctypes.byref(handle.c), _ptr(error_word), _stream()),
+           "moe_dispatch_noalloc")
+    return bufs, handle
 
 
 def moe_poll_error(ctx):

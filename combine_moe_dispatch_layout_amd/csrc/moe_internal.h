@@ -155,5 +155,7 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, int chunks, int kmax, int
 // T <= kFusedMaxTokens); a summary block plus one block of `threads` (256 or
 // 1024) per token.
 hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8, hipStream_t s);
+// Zero `words` 32-bit words at p (a kernel, so that it can sit in a captured graph).
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s);
 
 }  // namespace moe

@@ -1069,6 +1069,11 @@ hipError_t combine_bwd_c(const CombineBwdArgs& a, int kmax, int waves, int max_b
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kBlockThreads) void k_zero_words(uint32_t* p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kBlockThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 // At least one block: block 0 of the dispatch kernel also writes the handle's
 // offsets and counts, which must happen even when there are no tokens.
 // max_blocks > 0 caps the grid (the kernels loop over their items).
@@ -1114,6 +1119,14 @@ hipError_t launch_ll_fused(const PackArgs& a, int chunks, int threads, bool fp8,
     MOE_LL_CASE(1, 512)   // longer rows, ll_bpt blocks per token
 #undef MOE_LL_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s) {
+    if (words <= 0) return hipSuccess;
+    int64_t blocks = (words + kBlockThreads - 1) / kBlockThreads;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(k_zero_words, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, p, words);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, int chunks, int kmax, int max_blocks, hipStream_t s) {

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -68,7 +69,13 @@ moe_status check_config(const moe_config* c, Geometry* g) {
     return MOE_OK;
 }
 
-// Workspace layout (device, one allocation, 256-byte aligned pieces).
+// Workspace layout (device, one allocation, 256-byte aligned pieces).  The
+// first pieces -- error word, arrival counter and the grand totals, sized for
+// the largest supported E + R -- sit at the same offsets for every
+// configuration, so that a workspace shared by calls of different
+// configurations (the allocation-free dispatch's static scratch) keeps the
+// words that must read zero at the start of a layout zero: each layout zeroes
+// the totals it used before it ends.
 struct Workspace {
     size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
         off_erank, off_srank, total;
@@ -86,6 +93,7 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     w.off_err = take(4);
     w.off_done = take(4);
+    w.off_grand_tot = take(4 * ((size_t)MOE_MAX_EXPERTS + MOE_MAX_RANKS));
     w.off_cnt_e = take(4 * (size_t)c->num_experts);
     w.off_cnt_r = take(4 * (size_t)c->num_ranks);
     w.off_eoff = take(4 * ((size_t)c->num_experts + 1));
@@ -93,7 +101,6 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     // per-tile counts in either arrangement (column by column, or tile by tile)
     w.off_tile_cnt = take(4 * std::max((size_t)tile_stride(g) * (c->num_experts + c->num_ranks),
                                        (size_t)g.ntiles_max * cnt_stride(c)));
-    w.off_grand_tot = take(4 * ((size_t)c->num_experts + c->num_ranks));
     w.off_erank = take(4 * (size_t)c->max_tokens * c->topk);
     w.off_srank = take(2 * (size_t)c->max_tokens * c->num_ranks);
     w.total = o;
@@ -190,7 +197,7 @@ const char* kernel_name(int id) {
 }
 
 // Record timing events around one launch when timing is on; log it when asked.
-// ctx may be NULL: then nothing is recorded.
+// ctx may be NULL (the allocation-free dispatch): then nothing is recorded.
 struct TimedLaunch {
     moe_ctx* ctx;
     hipStream_t s;
@@ -212,7 +219,8 @@ struct TimedLaunch {
 };
 
 // What the launches of one call need besides their arguments: the
-// configuration, the device workspace, the error word and the launch tuning.
+// configuration, the device workspace (a context's, or the static scratch of
+// the allocation-free dispatch), the error word and the launch tuning.
 struct Exec {
     const moe_config* c;
     const Geometry* g;
@@ -794,3 +802,64 @@ MOE_API moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launc
     return st;
 }
 
+// ============================================================== allocation-free dispatch
+// Device scratch of moe_dispatch_noalloc: the layout workspace for callers
+// that cannot allocate.  One copy per GPU, loaded with the code object and
+// held until the process ends.  In host code `scratch` is only a stand-in for
+// the symbol: its device address, per device, comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of the scratch: on the first call on a device,
+// look up its address (with that device current) and zero its fixed header
+// (error word, arrival counter, grand totals) with a kernel on `s`, ahead of
+// the call's own launches; afterwards every layout leaves that header zero.
+moe_status scratch_for_device(int dev, const Workspace& wl, hipStream_t s, char** out) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+        if (launch_zero_words(static_cast<uint32_t*>(p), (int64_t)(wl.off_cnt_e / 4), s) != hipSuccess)
+            return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int64_t* topk_idx,
+                                        int32_t num_tokens, const moe_dispatch_buffers* bufs, moe_handle* handle,
+                                        uint32_t* error_word, void* stream) {
+    Geometry g;
+    moe_status st = check_config(cfg, &g);
+    if (st != MOE_OK) return st;
+    const Workspace wl = plan_workspace(cfg, g);
+    if (wl.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_CAPACITY;
+    st = check_dispatch_args(*cfg, x, topk_idx, num_tokens, bufs, handle);
+    if (st != MOE_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = nullptr;
+    st = scratch_for_device(dev, wl, s, &ws);
+    if (st != MOE_OK) return st;
+    Exec xc;
+    xc.c = cfg;
+    xc.g = &g;
+    xc.wl = &wl;
+    xc.ws = ws;
+    xc.err = error_word != nullptr ? error_word : reinterpret_cast<uint32_t*>(ws + wl.off_err);
+    xc.pack_chunks = 0;
+    xc.max_blocks = 0;
+    xc.ctx = nullptr;
+    int computed = -1;
+    return run_dispatch(xc, x, topk_idx, num_tokens, -1, bufs, handle, config_tag(cfg), s, &computed);
+}

@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define MOE_EP_ABI_VERSION 4   /* 3: moe_timing_launches; 4: stale-layout and non-finite
-                                  flags */
+                                  flags, moe_dispatch_noalloc */
 
 /* ---------------------------------------------------------------- status */
 typedef enum moe_status {
@@ -383,6 +383,30 @@ moe_status moe_timing_end(moe_ctx* ctx, double* total_ms, int64_t* launches);
  * open timing window or with NULL arrays for capacity > 0. */
 moe_status moe_timing_launches(moe_ctx* ctx, int32_t* kernel_ids, float* ms, int32_t capacity,
                                int32_t* count);
+
+/* ---------------------------------------------------------------- no allocation */
+/* For callers that cannot allocate device memory at all: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same result
+ * as moe_dispatch(reuse_layout = 0) on a context created with *cfg (the same
+ * rows, scales and handle arrays; the handle is accepted by moe_combine and
+ * the backward calls of any context with an equal configuration), without a
+ * context: the layout workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, loaded with the library and held until
+ * the process ends, and this call makes no allocation of any kind.
+ *   cfg         host; checked like moe_ctx_create.  MOE_ERR_CAPACITY when the
+ *               workspace it needs (MOE_BUF_WORKSPACE) exceeds the scratch.
+ *   x, topk_idx, num_tokens, bufs, handle: as in moe_dispatch.
+ *   error_word  device uint32, nullable: the kernels OR the moe_poll_error
+ *               bits into it (the caller clears it); NULL = not reported.
+ * The scratch keeps the last call's contents; the words that must start at
+ * zero are zeroed on the first call on each device and left zero by every
+ * call.  Calls that overlap on one GPU (other streams, other threads) race on
+ * the scratch and give wrong results: serialize them.  No launch tuning or
+ * workgroup cap applies, and no kernel timing is recorded. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int64_t* topk_idx,
+                                int32_t num_tokens, const moe_dispatch_buffers* bufs,
+                                moe_handle* handle, uint32_t* error_word, void* stream);
 
 #ifdef __cplusplus
 }

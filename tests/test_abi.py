@@ -132,6 +132,21 @@ def test_null_arguments_rejected(lib):
     assert lib.moe_timing_launches(None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_noalloc_host_checks_without_gpu(lib):
+    """moe_dispatch_noalloc checks its configuration, the scratch bound and its
+    arguments on the host before any HIP call."""
+    null = (None, None, 0, None, None, None, None)
+    assert lib.moe_dispatch_noalloc(None, *null) == moe.MOE_ERR_INVALID_ARG
+    big = moe.make_config(1 << 17, 256, 256, 64, 16, 0, 0, 0)    # workspace above the static scratch
+    assert moe.moe_size_hint(big, moe.MOE_BUF_WORKSPACE) > 8 << 20
+    assert lib.moe_dispatch_noalloc(ctypes.byref(big), *null) == moe.MOE_ERR_CAPACITY
+    ok = moe.make_config(4096, 7168, 256, 32, 8, 0, 0, 0)
+    assert moe.moe_size_hint(ok, moe.MOE_BUF_WORKSPACE) <= 8 << 20
+    assert lib.moe_dispatch_noalloc(ctypes.byref(ok), *null) == moe.MOE_ERR_INVALID_ARG
+    bad = moe.make_config(4096, 7168, 250, 32, 8, 0, 0, 0)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(bad), *null) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_product_does_not_reference_oracle():
     """The product package never imports, loads or links the oracle."""
     pkg = os.path.join(ROOT, "combine_moe_dispatch_layout_amd")
