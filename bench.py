@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="prefill",
                    choices=["tiny", "decode", "prefill", "grouped", "skewed"])
+    p.add_argument("--tokens", type=int, default=None,
+                   help="override the workload's token count (same shapes and routing recipe otherwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="skip the 128-token decode side measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward side measurement")
@@ -57,6 +59,9 @@ def parse():
                    help="host CPU time the oracle baseline runs for (whole steps, at least 3)")
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + steps only (for rocprofv3), print the JSON line without baselines")
+    p.add_argument("--protocol", default="cold", choices=["cold", "warm"],
+                   help="cold (default, the headline): a 1 GiB write flush before every step; warm: no flush "
+                        "(steps back to back, for profiling the kernels with warm caches)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run five 1 GiB device-to-device copies (known bytes) so that rocprofv3 "
                         "FETCH_SIZE / WRITE_SIZE counters can be scaled")
@@ -575,7 +580,7 @@ def main():
     moe.load_library()
     torch.cuda.set_device(0)
 
-    s = setup(moe, W, torch, a.workload)
+    s = setup(moe, W, torch, a.workload, T=a.tokens)
     c = s["c"]
     T = c["T"]
     if a.step == "backward":
@@ -593,11 +598,12 @@ def main():
     step_bytes = sum(alg.values())
     # the headline: W + K steps, each after a 1 GiB write flush, K of them timed with events
     flushes = make_flushes(torch)
-    cold_ms, cold_wall = timed_cold(moe, torch, s, a.steps, a.warmup, flushes["cold"], fn=fn)
+    head_flush = flushes["cold"] if a.protocol == "cold" else (lambda: None)
+    cold_ms, cold_wall = timed_cold(moe, torch, s, a.steps, a.warmup, head_flush, fn=fn)
     ms_per_step = sum(cold_ms) / len(cold_ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # per-kernel durations (library events), cold; warm (back to back) and after a read flush beside
-    passes = {"cold": timed_kernels(moe, torch, s, a.steps, flush=flushes["cold"], fn=fn)}
+    passes = {"cold": timed_kernels(moe, torch, s, a.steps, flush=head_flush, fn=fn)}
     warm = None
     if not a.profile_only:
         wall = timed(moe, torch, s, a.steps, a.warmup, fn=fn)
@@ -621,8 +627,10 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "protocol": "cold: a 1 GiB buffer rewritten (untimed) before every warm-up and timed step; "
-                    "per-step HIP events on the launch stream; value = bytes / mean step",
+        "protocol": ("cold: a 1 GiB buffer rewritten (untimed) before every warm-up and timed step; "
+                     "per-step HIP events on the launch stream; value = bytes / mean step"
+                     if a.protocol == "cold" else
+                     "warm (profiling run): steps back to back with per-step HIP events; value = bytes / mean step"),
         "us_per_step_p10_p50_p90": percentiles_us(cold_ms),
         "timed_loop_s_with_flushes": round(cold_wall, 4),
         "warm": warm,

@@ -722,14 +722,18 @@ __global__ __launch_bounds__(NT) void k_ll_dispatch(PackArgs a) {
     const int e = mine >= 0 && mine < E ? (int)mine : -1;   // lane j < k: expert of slot j
 
     // ---- this wavefront's share of the two counts, for every slot of the token
+    // (entry group u holds entries u * NT .. u * NT + NT - 1: groups at or past
+    // T * k hold none, groups at or past this token's first entry none of the
+    // earlier ones -- both limits are uniform, so those ballots are skipped)
     for (int j = 0; j < k; ++j) {
         const int ej = readlane(e, j);
         if (ej < 0) continue;
         int c_hb = 0, c_lt = 0;
 #pragma unroll
         for (int u = 0; u < kPerThread; ++u) {
+            if (u * NT >= nent) break;
             const int i = u * NT + tid;
-            c_hb += __popcll(__ballot(ent[u] == ej && i < before));
+            if (u * NT < before) c_hb += __popcll(__ballot(ent[u] == ej && i < before));
             c_lt += __popcll(__ballot(ent[u] >= 0 && ent[u] < ej));
         }
         if (lane == 0) {
