@@ -209,8 +209,11 @@ def setup(moe, W, torch, name, T=None):
 
 
 def step(moe, s):
-    """Layout, dispatch reusing that layout, combine (the normal-mode call sequence)."""
-    moe.moe_dispatch_layout(s["ctx"], s["idx"], s["cnt_e"], s["cnt_r"], s["in_rank"])
+    """Layout, dispatch reusing that layout, combine (the normal-mode call
+    sequence).  The layout call is given x, so that its launch also reads the
+    token rows into the Infinity Cache for the dispatch
+    (moe_dispatch_layout_prefetch)."""
+    moe.moe_dispatch_layout(s["ctx"], s["idx"], s["cnt_e"], s["cnt_r"], s["in_rank"], x=s["x"])
     moe.moe_dispatch(s["ctx"], s["x"], s["idx"], reuse_layout=True, bufs=s["bufs"], handle=s["h"])
     moe.moe_combine(s["ctx"], s["y"], s["w"], s["h"], out=s["out"])
 
@@ -594,7 +597,7 @@ def main():
         if fn is step_ll:
             alg["layout"] = 0                     # the routing is read inside the fused dispatch
         step_desc = ("dispatch from topk_idx (fused) + combine" if fn is step_ll
-                     else "layout + dispatch(reuse layout) + combine")
+                     else "layout (reading x into the Infinity Cache meanwhile) + dispatch(reuse layout) + combine")
     step_bytes = sum(alg.values())
     # the headline: W + K steps, each after a 1 GiB write flush, K of them timed with events
     flushes = make_flushes(torch)
@@ -655,6 +658,9 @@ def main():
                      "frac_warm": (round(per_kernel[dom]["GB/s_warm"] / HBM_PEAK_GBS, 4)
                                    if "GB/s_warm" in per_kernel[dom] else None),
                      "alg_bytes_per_launch": per_kernel[dom]["alg_bytes"],
+                     "note": ("the layout launch before the dispatch reads x into the Infinity Cache "
+                              "(moe_dispatch_layout_prefetch), so the dispatch's cold reads of x hit there; "
+                              "the step value counts the layout's time for it" if fn is step else None),
                      "us_per_launch": per_kernel[dom]["us"],
                      "traffic": traffic_for(dom, a.workload + ("_backward" if a.step == "backward" else ""))},
     }

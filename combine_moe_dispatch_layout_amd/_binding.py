@@ -76,7 +76,8 @@ EXPORTS = ("moe_status_str", "moe_size_hint", "moe_ctx_create", "moe_ctx_destroy
            "moe_ctx_tune", "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_backward",
            "moe_combine_backward", "moe_ctx_set_max_workgroups", "moe_hook_create", "moe_hook_destroy",
            "moe_hook_record", "moe_hook_wait", "moe_poll_error", "moe_timing_begin", "moe_timing_end",
-           "moe_timing_launches", "moe_dispatch_noalloc")
+           "moe_timing_launches", "moe_dispatch_noalloc",
+           "moe_dispatch_layout_prefetch")
 
 _lib = None
 
@@ -100,6 +101,7 @@ def load_library(path=LIB_PATH):
         "moe_ctx_config": [vp, ctypes.POINTER(moe_config)],
         "moe_ctx_tune": [vp, i32, i32],
         "moe_dispatch_layout": [vp, vp, i32, vp, vp, vp, vp],
+        "moe_dispatch_layout_prefetch": [vp, vp, i32, vp, vp, vp, vp, vp],
         "moe_dispatch": [vp, vp, vp, i32, i32, ctypes.POINTER(moe_dispatch_buffers),
                          ctypes.POINTER(moe_handle), vp],
         "moe_combine": [vp, vp, vp, ctypes.POINTER(moe_handle), vp, vp],
@@ -365,9 +367,11 @@ def _check_bufs(ctx, b):
 
 
 def moe_dispatch_layout(ctx, topk_idx, num_tokens_per_expert=None, num_tokens_per_rank=None,
-                        is_token_in_rank=None):
+                        is_token_in_rank=None, x=None):
     """Returns (num_tokens_per_expert int32[E], num_tokens_per_rank int32[R],
-    is_token_in_rank uint8[T, R])."""
+    is_token_in_rank uint8[T, R]).  x: the bf16 token rows [T, H] of the
+    dispatch that will reuse this layout; given, the same launch reads them
+    into the Infinity Cache (moe_dispatch_layout_prefetch)."""
     c = ctx.cfg
     _as_dev(topk_idx, torch.int64, "topk_idx")
     T = topk_idx.shape[0]
@@ -383,9 +387,17 @@ def moe_dispatch_layout(ctx, topk_idx, num_tokens_per_expert=None, num_tokens_pe
     _out(num_tokens_per_expert, torch.int32, c.num_experts, "num_tokens_per_expert")
     _out(num_tokens_per_rank, torch.int32, c.num_ranks, "num_tokens_per_rank")
     _out(is_token_in_rank, torch.uint8, T * c.num_ranks, "is_token_in_rank")
-    _check(load_library().moe_dispatch_layout(
-        ctx.handle, _ptr(topk_idx), T, _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
-        _ptr(is_token_in_rank), _stream()), "moe_dispatch_layout")
+    if x is None:
+        _check(load_library().moe_dispatch_layout(
+            ctx.handle, _ptr(topk_idx), T, _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
+            _ptr(is_token_in_rank), _stream()), "moe_dispatch_layout")
+    else:
+        _as_dev(x, torch.bfloat16, "x")
+        if x.dim() != 2 or tuple(x.shape) != (T, c.hidden):
+            raise ValueError("x must be [T, %d]" % c.hidden)
+        _check(load_library().moe_dispatch_layout_prefetch(
+            ctx.handle, _ptr(topk_idx), T, _ptr(x), _ptr(num_tokens_per_expert), _ptr(num_tokens_per_rank),
+            _ptr(is_token_in_rank), _stream()), "moe_dispatch_layout_prefetch")
     return num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank
 
 

@@ -82,6 +82,12 @@ struct LayoutArgs {
     uint8_t* out_in_rank;      // [T, R]
     uint32_t* err;
     uint32_t* done;            // arrival counter of the tile blocks (reset by the last one)
+    int32_t ntiles;            // workgroups 0 .. ntiles-1 are the layout's tiles
+    // workgroups ntiles .. gridDim.x-1 read these bytes (the token rows of the
+    // dispatch that follows) so that they sit in the Infinity Cache when it runs
+    const void* warm;
+    int64_t warm_chunks;       // 16-byte chunks at `warm`
+    uint32_t* warm_sink;       // written only if the loaded bits hit one value (keeps the loads)
 };
 
 struct PackArgs {
@@ -144,7 +150,8 @@ struct CombineBwdArgs {
 };
 
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
-hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s);
+// ntiles layout workgroups plus warm_blocks workgroups reading a.warm.
+hipError_t launch_layout(const LayoutArgs& a, int ntiles, int warm_blocks, hipStream_t s);
 // chunks: 16-byte input chunks each lane handles per work item (1,2,4,8,16).
 // max_blocks > 0 caps the grid; the kernels then loop over their work items.
 hipError_t launch_pack(const PackArgs& a, int chunks, bool fp8, bool ll, bool send, int max_blocks,

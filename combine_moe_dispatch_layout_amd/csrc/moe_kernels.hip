@@ -168,7 +168,27 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(LayoutArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int E = a.E, R = a.R, k = a.k;
-    const int ntiles = gridDim.x;
+    const int ntiles = a.ntiles;
+    if ((int)blockIdx.x >= ntiles) {
+        // ---- the layout occupies a few compute units for several microseconds
+        // of dependent latencies while HBM sits idle: the other workgroups read
+        // the token rows the dispatch will read next, so that they come from
+        // the Infinity Cache then instead of HBM.  Cached loads (they allocate
+        // in the caches); the bits are folded into one word that is stored
+        // only if it hits one value, so that the loads are kept.
+        const u32x4* p = static_cast<const u32x4*>(a.warm);
+        const int64_t stride = (int64_t)(gridDim.x - ntiles) * kLayoutThreads;
+        uint32_t acc = 0u;
+        for (int64_t i = (int64_t)(blockIdx.x - ntiles) * kLayoutThreads + tid; i < a.warm_chunks; i += 8 * stride) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = i + u * stride < a.warm_chunks ? p[i + u * stride] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
+        }
+        if (acc == 0x9e3779b9u) *a.warm_sink = acc;
+        return;
+    }
     const int64_t tok0 = (int64_t)blockIdx.x * kTileTokens + w * kWaveTokens;   // this wave's first token
     const int64_t t = tok0 + lane;          // lane = token of the wave (lanes < kWaveTokens)
     const bool tok_ok = lane < kWaveTokens && t < a.T;
@@ -1089,11 +1109,14 @@ dim3 items_grid(int64_t items, int64_t max_blocks, int waves_per_block = kWavesP
 
 }  // namespace
 
-hipError_t launch_layout(const LayoutArgs& a, int ntiles, hipStream_t s) {
-    if (ntiles < 1 || a.mode != layout_mode(ntiles)) return hipErrorInvalidValue;
-    if (a.k <= 8) hipLaunchKernelGGL(k_layout<8>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
-    else if (a.k <= 16) hipLaunchKernelGGL(k_layout<16>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_layout<32>, dim3(ntiles), dim3(kLayoutThreads), 0, s, a);
+hipError_t launch_layout(const LayoutArgs& a, int ntiles, int warm_blocks, hipStream_t s) {
+    if (ntiles < 1 || a.ntiles != ntiles || a.mode != layout_mode(ntiles) || warm_blocks < 0 ||
+        (warm_blocks > 0 && (a.warm == nullptr || a.warm_sink == nullptr)))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(ntiles + warm_blocks));
+    if (a.k <= 8) hipLaunchKernelGGL(k_layout<8>, grid, dim3(kLayoutThreads), 0, s, a);
+    else if (a.k <= 16) hipLaunchKernelGGL(k_layout<16>, grid, dim3(kLayoutThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_layout<32>, grid, dim3(kLayoutThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ moe_status check_config(const moe_config* c, Geometry* g) {
 // words that must read zero at the start of a layout zero: each layout zeroes
 // the totals it used before it ends.
 struct Workspace {
-    size_t off_err, off_done, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
+    size_t off_err, off_done, off_sink, off_cnt_e, off_cnt_r, off_eoff, off_roff, off_tile_cnt, off_grand_tot,
         off_erank, off_srank, total;
 };
 
@@ -93,6 +93,7 @@ Workspace plan_workspace(const moe_config* c, const Geometry& g) {
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     w.off_err = take(4);
     w.off_done = take(4);
+    w.off_sink = take(4);
     w.off_grand_tot = take(4 * ((size_t)MOE_MAX_EXPERTS + MOE_MAX_RANKS));
     w.off_cnt_e = take(4 * (size_t)c->num_experts);
     w.off_cnt_r = take(4 * (size_t)c->num_ranks);
@@ -250,12 +251,41 @@ Exec ctx_exec(moe_ctx* ctx) {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Compute units of a device (cached per device; 0 if the query fails).
+int device_cus(int dev) {
+    static std::mutex mu;
+    static int cus[64];
+    if (dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Token rows of at least this many bytes are read into the Infinity Cache
+// during the layout; at most this many (the first rows, which the dispatch
+// reads first; the cache is 256 MB).
+constexpr int64_t kWarmMinBytes = 2ll << 20;
+constexpr int64_t kWarmMaxBytes = 96ll << 20;
+
 // Count + scan launch into the workspace.  *mode receives the layout mode it
 // ran in (the dispatch that consumes this layout is told the same mode).
+// warm_x (nullable): the bf16 token rows [T, H] of the dispatch that follows;
+// the compute units the layout leaves idle read them meanwhile (see k_layout).
 moe_status run_layout(const Exec& x, const int64_t* topk_idx, int32_t T, int32_t* out_cnt_e,
-                      int32_t* out_cnt_r, uint8_t* out_in_rank, hipStream_t s, int* mode) {
+                      int32_t* out_cnt_r, uint8_t* out_in_rank, const void* warm_x, hipStream_t s, int* mode) {
     const moe_config& c = *x.c;
     const int ntiles = std::max(1, (T + kTileTokens - 1) / kTileTokens);
+    int warm_blocks = 0;
+    int64_t warm_bytes = warm_x != nullptr ? std::min<int64_t>((int64_t)T * c.hidden * 2, kWarmMaxBytes) : 0;
+    if (warm_bytes >= kWarmMinBytes) {
+        int dev = -1;
+        (void)hipGetDevice(&dev);
+        warm_blocks = std::max(0, device_cus(dev) - ntiles);
+    }
+    if (warm_blocks == 0) warm_bytes = 0;
     LayoutArgs a;
     a.topk_idx = topk_idx;
     a.T = T;
@@ -283,8 +313,12 @@ moe_status run_layout(const Exec& x, const int64_t* topk_idx, int32_t T, int32_t
     a.out_in_rank = out_in_rank;
     a.err = x.err;
     a.done = x.u32(x.wl->off_done);
+    a.ntiles = ntiles;
+    a.warm = warm_x;
+    a.warm_chunks = warm_bytes / 16;
+    a.warm_sink = x.u32(x.wl->off_sink);
     TimedLaunch tl(x.ctx, s, MOE_KERNEL_LAYOUT);
-    hipError_t e = launch_layout(a, ntiles, s);
+    hipError_t e = launch_layout(a, ntiles, warm_blocks, s);
     tl.done();
     *mode = a.mode;
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -329,7 +363,7 @@ moe_status run_dispatch(const Exec& xc, const void* x, const int64_t* topk_idx, 
                        num_tokens <= kFusedMaxTokens;
     int mode = reuse_mode;
     if (reuse_mode < 0 && !fused) {
-        moe_status st = run_layout(xc, topk_idx, num_tokens, nullptr, nullptr, nullptr, s, &mode);
+        moe_status st = run_layout(xc, topk_idx, num_tokens, nullptr, nullptr, nullptr, x, s, &mode);
         if (st != MOE_OK) return st;
         *new_layout_mode = mode;
     }
@@ -569,22 +603,42 @@ MOE_API moe_status moe_hook_wait(const moe_hook* hook, void* stream) {
                                                                                                  : MOE_ERR_HIP;
 }
 
-MOE_API moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
-                                       int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank,
-                                       uint8_t* is_token_in_rank, void* stream) {
+namespace {
+
+moe_status layout_call(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens, const void* x,
+                       int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank, uint8_t* is_token_in_rank,
+                       void* stream) {
     if (ctx == nullptr || !on_ctx_device(ctx)) return MOE_ERR_INVALID_ARG;
     if (num_tokens < 0) return MOE_ERR_INVALID_ARG;
     if (num_tokens > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
     if (num_tokens > 0 && topk_idx == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
     int mode = -1;
     const moe_status st = run_layout(ctx_exec(ctx), topk_idx, num_tokens, num_tokens_per_expert,
-                                     num_tokens_per_rank, is_token_in_rank, reinterpret_cast<hipStream_t>(stream),
+                                     num_tokens_per_rank, is_token_in_rank, x, reinterpret_cast<hipStream_t>(stream),
                                      &mode);
     ctx->layout_valid = st == MOE_OK;
     ctx->layout_idx = topk_idx;
     ctx->layout_T = num_tokens;
     ctx->layout_mode = mode;
     return st;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
+                                       int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank,
+                                       uint8_t* is_token_in_rank, void* stream) {
+    return layout_call(ctx, topk_idx, num_tokens, nullptr, num_tokens_per_expert, num_tokens_per_rank,
+                       is_token_in_rank, stream);
+}
+
+MOE_API moe_status moe_dispatch_layout_prefetch(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
+                                                const void* x, int32_t* num_tokens_per_expert,
+                                                int32_t* num_tokens_per_rank, uint8_t* is_token_in_rank,
+                                                void* stream) {
+    return layout_call(ctx, topk_idx, num_tokens, x, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
+                       stream);
 }
 
 MOE_API moe_status moe_dispatch(moe_ctx* ctx, const void* x, const int64_t* topk_idx, int32_t num_tokens,

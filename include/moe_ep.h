@@ -53,8 +53,8 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 4   /* 3: moe_timing_launches; 4: stale-layout and non-finite
-                                  flags, moe_dispatch_noalloc */
+#define MOE_EP_ABI_VERSION 5   /* 3: moe_timing_launches; 4: stale-layout and non-finite
+                                  flags, moe_dispatch_noalloc; 5: moe_dispatch_layout_prefetch */
 
 /* ---------------------------------------------------------------- status */
 typedef enum moe_status {
@@ -189,6 +189,23 @@ moe_status moe_ctx_tune(moe_ctx* ctx, int32_t dispatch_chunks, int32_t combine_c
 moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
                                int32_t* num_tokens_per_expert, int32_t* num_tokens_per_rank,
                                uint8_t* is_token_in_rank, void* stream);
+
+/* The dispatch layout, plus a read of the token rows the dispatch reusing
+ * this layout will copy (an MI355X-specific addition; the pages' layout call
+ * takes topk_idx only).  The layout runs on one workgroup per 256 tokens and is
+ * bound by dependent latencies for several microseconds, while HBM is idle; the
+ * launch's other workgroups, on the compute units the layout leaves free, read
+ * x meanwhile (its first 96 MB), so that the dispatch finds those rows in the
+ * 256 MB Infinity Cache instead of HBM.  Outputs, checks and the reused state
+ * are those of moe_dispatch_layout; results are identical.
+ *   x   bf16 [num_tokens, H], 16-byte aligned, only read; NULL = exactly
+ *       moe_dispatch_layout.  Rows of under 2 MB in all are not read.
+ * moe_dispatch with reuse_layout = 0 does the same inside its own layout
+ * launch. */
+moe_status moe_dispatch_layout_prefetch(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
+                                        const void* x, int32_t* num_tokens_per_expert,
+                                        int32_t* num_tokens_per_rank, uint8_t* is_token_in_rank,
+                                        void* stream);
 
 /* ---------------------------------------------------------------- dispatch */
 /* Output buffers of one dispatch (host struct of device pointers).

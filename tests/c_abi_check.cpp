@@ -116,7 +116,8 @@ int main() {
 
     hipStream_t s;
     HIPCHK(hipStreamCreate(&s));
-    API(moe_dispatch_layout(ctx, idx, T, cnt_e, cnt_r, in_rank, s));
+    // the layout with the token rows read into the Infinity Cache meanwhile (same outputs)
+    API(moe_dispatch_layout_prefetch(ctx, idx, T, x, cnt_e, cnt_r, in_rank, s));
     moe_dispatch_buffers bufs = {send, nullptr, recv, nullptr};
     API(moe_dispatch(ctx, x, idx, T, 1, &bufs, &h, s));
     // identity expert: the expert outputs are the received rows themselves

@@ -117,6 +117,7 @@ def test_null_arguments_rejected(lib):
     assert lib.moe_size_hint(None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_ctx_destroy(None) == moe.MOE_OK
     assert lib.moe_dispatch_layout(None, None, 0, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_layout_prefetch(None, None, 0, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(None, None, None, 0, 0, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(None, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG

@@ -56,15 +56,16 @@ def poison(bufs):
 
 
 def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, check_poison=True,
-             tag="", max_workgroups=0, side_stream=False, tune=None, ctx=None):
+             tag="", max_workgroups=0, side_stream=False, tune=None, ctx=None, prefetch=False):
     """Layout + dispatch + combine on the GPU and in the oracle; compare all.
-    ctx: an existing context to run on (kept open), else a fresh one."""
+    ctx: an existing context to run on (kept open), else a fresh one.
+    prefetch: give the layout call x (moe_dispatch_layout_prefetch)."""
     T = idx.shape[0]
     ll = c["layout"] == W.LAYOUT_PADDED_LL
     fp8 = c["quant"] == W.QUANT_FP8
-    log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d max_wg=%d side=%s" %
+    log("case %s: T=%d H=%d E=%d R=%d k=%d quant=%d layout=%d reuse=%s s0=%d max_wg=%d side=%s prefetch=%s" %
         (tag, T, c["H"], c["E"], c["R"], c["k"], c["quant"], c["layout"], reuse, src_rank, max_workgroups,
-         side_stream))
+         side_stream, prefetch))
     own_ctx = ctx is None
     if own_ctx:
         ctx = make_ctx(gpu, c, T, max_tokens, src_rank)
@@ -84,7 +85,7 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
     h.pos.fill_(-7)
 
     # ---- layout
-    cnt_e, cnt_r, in_rank = gpu.moe_dispatch_layout(ctx, idx_d)
+    cnt_e, cnt_r, in_rank = gpu.moe_dispatch_layout(ctx, idx_d, x=x if prefetch else None)
     # ---- dispatch (optionally issued on a side stream and completed by a hook)
     if side_stream:
         side = torch.cuda.Stream()
@@ -188,6 +189,26 @@ def run_case(gpu, c, x_bits, idx, w, reuse=True, max_tokens=None, src_rank=0, ch
 def test_workload_full_size(gpu, name):
     d = W.make(name)
     run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], reuse=True, tag=name)
+
+
+@pytest.mark.parametrize("name", ["prefill", "grouped", "skewed", "tiny"])
+def test_workload_layout_with_prefetch(gpu, name):
+    """The layout launch that also reads x into the Infinity Cache gives the
+    same layout (full size: the extra workgroups run; tiny: below the size at
+    which they are launched)."""
+    d = W.make(name)
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], reuse=True, tag=name + "-prefetch",
+             prefetch=True)
+
+
+@pytest.mark.parametrize("T", [1, 300, 17000])
+def test_layout_prefetch_ragged(gpu, T):
+    """Ragged batches through the prefetching layout: one tile, per-tile sums,
+    stored per-tile prefixes (x of 17000 tokens is larger than the part read)."""
+    c = small_cfg("prefill", H=4096)
+    d = W.make("prefill", T=T)
+    run_case(gpu, c, d["x"][:, :4096].copy(), d["topk_idx"], d["topk_weights"], max_tokens=T,
+             tag="prefetch-ragged", prefetch=True)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "grouped"])
