@@ -18,11 +18,13 @@
 //    128-channel block), then stored with 16-byte (8-byte for fp8) stores to
 //    every destination row: up to min(k, R) send rows and k receive rows.
 //    Destination row indices are wave-uniform (readlane -> SGPR), so the store
-//    loop has no divergence.  Rows are written with non-temporal stores, one
-//    16-byte chunk per lane per work item: on MI355X this beats cached stores
-//    by 4% (prefill), 30% (fp8 grouped) and 10% (skewed) on its own, and cached
-//    stores would push ~0.9 GB per prefill launch through the 256 MB Infinity
-//    Cache, slowing a concurrent bf16 GEMM by 1.3x (its operands are evicted).
+//    loop has no divergence.  Rows are written with non-temporal stores at
+//    system scope (buffer stores, sc0 sc1 nt), one 16-byte chunk per lane per
+//    work item: on MI355X non-temporal beats cached stores by 4% (prefill), 30%
+//    (fp8 grouped) and 10% (skewed) on its own, and cached stores would push
+//    ~0.9 GB per prefill launch through the 256 MB Infinity Cache, slowing a
+//    concurrent bf16 GEMM by 1.3x (its operands are evicted); the system scope
+//    leaves fewer dirty lines to write back when the launch ends.
 //  * Combine: one wavefront per (token, row slice); all k routed rows of the
 //    slice are loaded before any arithmetic, accumulated in fp32 in slot order
 //    with separately rounded multiply and add, rounded once to bf16 (RNE).  The
@@ -398,15 +400,29 @@ __device__ __forceinline__ ChunkState chunk_state(int64_t gi, int64_t nchunk) {
 }
 
 // ============================================================== dispatch
-// Store a slice (C chunks per lane) of one row.
+// Cache policy of the dispatch's row stores (the cache-policy operand of the
+// gfx950 buffer store: bit 0 sc0, bit 1 nt, bit 4 sc1): non-temporal at
+// system scope (sc0 sc1 nt).  Measured on MI355X against plain non-temporal
+// stores (dispatch, after a 1 GiB write flush): prefill 180 -> 176 us, skewed
+// 118 -> 115 us, grouped fp8 81 -> 80 us, and the decode step 10.65 -> 9.8 us
+// graph-replayed (the launch ends with fewer dirty lines to write back).
+// System scope without nt makes the rows allocate in the Infinity Cache:
+// prefill 171 us, but skewed 124 us and grouped fp8 98 us, so nt stays.
+constexpr int kStoreRows = 0x13;   // sc0 sc1 nt
+
+// Store a slice (C chunks per lane) of one row of nchunk chunks: buffer stores
+// over the row (a chunk past its end falls out of the buffer and is dropped by
+// the hardware).
 template <int C, typename V>
 __device__ __forceinline__ void store_row(V* dst, const V* v, int64_t gbase, int lane, int64_t nchunk) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)(nchunk * sizeof(V)), 0x00020000);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int64_t gi = gbase + i * 64;
-        const ChunkState cs = chunk_state(gi, nchunk);
-        if (cs == kChunkFull) __builtin_nontemporal_store(v[i], dst + gi + lane);
-        else if (cs == kChunkPart && gi + lane < nchunk) __builtin_nontemporal_store(v[i], dst + gi + lane);
+        if (chunk_state(gi, nchunk) == kChunkNone) continue;
+        const int off = (int)((gi + lane) * sizeof(V));
+        if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, off, 0, kStoreRows);
+        else __builtin_amdgcn_raw_buffer_store_b64(v[i], r, off, 0, kStoreRows);
     }
 }
 
