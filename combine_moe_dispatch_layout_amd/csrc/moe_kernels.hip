@@ -889,7 +889,11 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
     const int64_t nchunk = a.H / 8;
     const int64_t g0 = (int64_t)s * 64 * C + lane;
     const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.y);
-    u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.out) + (int64_t)t * nchunk;
+    // output row as a buffer: non-temporal stores at system scope (as the
+    // dispatch's rows; decode step 9.8 -> 9.6 us, prefill unchanged); a chunk
+    // past the row end falls out of it
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<u32x4*>(a.out) + (int64_t)t * nchunk, 0, (int)(nchunk * 16), 0x00020000);
     if (C * KMAX <= 16 && g0 - lane + C * 64 <= nchunk) {
         // whole slice inside the row: every load of the slice is issued before
         // any arithmetic, so that all C * k row chunks are in flight at once
@@ -903,7 +907,9 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
             for (int i = 0; i < C; ++i)
                 if (pj[j] >= 0) v[i][j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g0 + i * 64);
 #pragma unroll
-        for (int i = 0; i < C; ++i) __builtin_nontemporal_store(combine_chunk<KMAX>(v[i], pj, wj), out + g0 + i * 64);
+        for (int i = 0; i < C; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(combine_chunk<KMAX>(v[i], pj, wj), out, (int)((g0 + i * 64) * 16), 0,
+                                                   kStoreRows);
         return;
     }
 #pragma unroll
@@ -915,7 +921,7 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t item,
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
                 if (pj[j] >= 0) v[j] = __builtin_nontemporal_load(y + (int64_t)pj[j] * nchunk + g);
-            __builtin_nontemporal_store(combine_chunk<KMAX>(v, pj, wj), out + g);
+            __builtin_amdgcn_raw_buffer_store_b128(combine_chunk<KMAX>(v, pj, wj), out, (int)(g * 16), 0, kStoreRows);
         }
     }
 }
