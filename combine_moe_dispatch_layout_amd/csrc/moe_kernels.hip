@@ -23,8 +23,9 @@
 //    work item: on MI355X non-temporal beats cached stores by 4% (prefill), 30%
 //    (fp8 grouped) and 10% (skewed) on its own, and cached stores would push
 //    ~0.9 GB per prefill launch through the 256 MB Infinity Cache, slowing a
-//    concurrent bf16 GEMM by 1.3x (its operands are evicted); the system scope
-//    leaves fewer dirty lines to write back when the launch ends.
+//    concurrent bf16 GEMM by 1.3x (its operands are evicted); among the
+//    non-temporal forms, system scope measured never slower and up to 3 us
+//    faster per launch.
 //  * Combine: one wavefront per (token, row slice); all k routed rows of the
 //    slice are loaded before any arithmetic, accumulated in fp32 in slot order
 //    with separately rounded multiply and add, rounded once to bf16 (RNE).  The
