@@ -34,9 +34,13 @@
  *    one stream at a time; it is not thread-safe.  Calls made on another
  *    device return MOE_ERR_INVALID_ARG.
  *  - Argument errors are reported synchronously by the return value and leave
- *    nothing enqueued.  Data errors found by the kernels (an expert id outside
- *    [-1, E)) are recorded in a sticky device word that moe_poll_error reads;
- *    the offending slot is then treated as empty (-1).
+ *    nothing enqueued.  Data errors found by the kernels are recorded in a
+ *    sticky device word that moe_poll_error reads: an expert id outside
+ *    [-1, E) (the slot is treated as empty, -1), a row index outside its
+ *    buffer or a low-latency window overflow (the row is not placed), a reused
+ *    layout made from other routing (the changed tokens are dropped, see
+ *    moe_dispatch) and Inf or NaN in an fp8 dispatch (those blocks'
+ *    codes and scales are unspecified).
  *  - bf16 buffers are passed as raw 16-bit storage; fp8 buffers hold OCP
  *    E4M3FN codes, one byte per channel.
  *  - With MOE_EP_LOG=1 in the environment when a context is created, each
