@@ -21,7 +21,7 @@ with no flush ("warm") are reported beside it.  The per-kernel roofline uses
 durations measured with HIP events the library records on its own launch
 stream around each kernel (moe_timing_begin / moe_timing_end), cold.
 
-Prints ONE JSON line.  --gpus N with N > 1 is refused: this build drives one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 is refused: the library drives one GPU.
 """
 import argparse
 import hashlib
@@ -563,7 +563,7 @@ def oracle_timing(s, runs=None, seconds=None, min_runs=3, max_runs=100000):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py drives a single GPU: this build has no multi-GPU path "
+        print("bench.py drives a single GPU: the library has no multi-GPU path "
               "(peer transport is replaced by a local copy); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
