@@ -403,7 +403,7 @@ def overlap(moe, torch, s, fn, caps, iters=40):
 
 
 def copy_reference(torch, nbytes=1 << 30, reps=20):
-    """Achievable HBM rate of a plain 1 GiB device-to-device copy on this machine
+    """Achievable HBM rate of a plain 1 GiB device-to-device copy on this GPU
     (read + write bytes / time, HIP events on the current stream)."""
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
