@@ -696,6 +696,13 @@ def main():
         ll_bytes = alg_d["dispatch"] + alg_d["combine"]      # routing is read inside dispatch
         warm_us = 1e6 * wall_d / 500
         graph_us = 1e6 * timed_graph(moe, torch, sd, step_ll)
+        # each call on its own, 100 of it captured in a graph: the GPU time of one
+        # call with no host launch overhead (kernel plus the boundary to the next)
+        graph_call_us = {
+            "dispatch": 1e6 * timed_graph(moe, torch, sd, lambda moe_, s_: moe_.moe_dispatch(
+                s_["ctx"], s_["x"], s_["idx"], reuse_layout=False, bufs=s_["bufs"], handle=s_["h"])),
+            "combine": 1e6 * timed_graph(moe, torch, sd, lambda moe_, s_: moe_.moe_combine(
+                s_["ctx"], s_["y"], s_["w"], s_["h"], out=s_["out"]))}
         # the same step through prepared calls (arguments marshalled once): what a
         # lean host loop sees, launch overhead included
         pd = moe.prepare_dispatch(sd["ctx"], sd["x"], sd["idx"], False, sd["bufs"], sd["h"])
@@ -720,6 +727,7 @@ def main():
             "step": "dispatch from topk_idx (one fused launch) + combine",
             "us_per_step_warm": round(warm_us, 2),
             "us_per_step_graph": round(graph_us, 2),
+            "us_per_call_graph": {k_: round(v, 2) for k_, v in graph_call_us.items()},
             "us_per_step_prepared_calls": round(prep_us, 2),
             "host_us_per_call": host_calls,
             "us_per_kernel_cold": {k_: round(v, 2) for k_, v in cold.items()},
