@@ -269,6 +269,8 @@ int device_cus(int dev) {
 // reads first; the cache is 256 MB).
 constexpr int64_t kWarmMinBytes = 2ll << 20;
 constexpr int64_t kWarmMaxBytes = 96ll << 20;
+// A workgroup cap counts 256-thread workgroups; the layout's are 512 threads.
+constexpr int kLayoutBlockUnits = 2;
 
 // Count + scan launch into the workspace.  *mode receives the layout mode it
 // ran in (the dispatch that consumes this layout is told the same mode).
@@ -284,6 +286,8 @@ moe_status run_layout(const Exec& x, const int64_t* topk_idx, int32_t T, int32_t
         int dev = -1;
         (void)hipGetDevice(&dev);
         warm_blocks = std::max(0, device_cus(dev) - ntiles);
+        // under a workgroup cap the extra workgroups stay within it too
+        if (x.max_blocks > 0) warm_blocks = std::min(warm_blocks, x.max_blocks / kLayoutBlockUnits);
     }
     if (warm_blocks == 0) warm_bytes = 0;
     LayoutArgs a;

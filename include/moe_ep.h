@@ -203,7 +203,9 @@ moe_status moe_dispatch_layout(moe_ctx* ctx, const int64_t* topk_idx, int32_t nu
  * 256 MB Infinity Cache instead of HBM.  Outputs, checks and the reused state
  * are those of moe_dispatch_layout; results are identical.
  *   x   bf16 [num_tokens, H], 16-byte aligned, only read; NULL = exactly
- *       moe_dispatch_layout.  Rows of under 2 MB in all are not read.
+ *       moe_dispatch_layout.  Rows of under 2 MB in all are not read.  Under
+ *       a workgroup cap (moe_ctx_set_max_workgroups) the extra workgroups,
+ *       512 threads each, stay within it (none below a cap of 2).
  * moe_dispatch with reuse_layout = 0 does the same inside its own layout
  * launch. */
 moe_status moe_dispatch_layout_prefetch(moe_ctx* ctx, const int64_t* topk_idx, int32_t num_tokens,
@@ -346,9 +348,11 @@ moe_status moe_combine_backward(moe_ctx* ctx, const void* grad_out, const float*
  * unchanged.  A workgroup is 256 threads for the dispatch and 64 threads per
  * row slice (up to 1024) for the combine backward; the combine and the
  * dispatch backward run one-wavefront workgroups, 4 * max_workgroups of them
- * (the wavefronts of max_workgroups 256-thread workgroups).  The layout
- * kernel (a few workgroups) and the fused low-latency dispatch (the pages:
- * low-latency kernels need no SM control) are not capped.  Capping leaves
+ * (the wavefronts of max_workgroups 256-thread workgroups).  The layout's
+ * tile workgroups (one per 256 tokens) and the fused low-latency dispatch
+ * (the pages: low-latency kernels need no SM control) are not capped; the
+ * extra workgroups a layout launch uses to read x are (512 threads each, so
+ * max_workgroups / 2 of them).  Capping leaves
  * compute units to kernels on other streams, e.g. GEMMs overlapped with
  * dispatch and combine. */
 moe_status moe_ctx_set_max_workgroups(moe_ctx* ctx, int32_t max_workgroups);

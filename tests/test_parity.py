@@ -518,6 +518,15 @@ def test_max_workgroups_full_prefill(gpu):
              max_workgroups=256)
 
 
+@pytest.mark.parametrize("max_wg", [1, 3, 64])
+def test_max_workgroups_with_prefetch(gpu, max_wg):
+    """The layout that also reads x under a workgroup cap (its extra
+    workgroups limited to the cap, none at a cap of 1): same results."""
+    d = W.make("prefill")
+    run_case(gpu, d["cfg"], d["x"], d["topk_idx"], d["topk_weights"], tag="maxwg-prefetch-%d" % max_wg,
+             max_workgroups=max_wg, prefetch=True)
+
+
 @pytest.mark.parametrize("name", ["prefill", "decode"])
 def test_hook_issue_complete(gpu, name):
     """Dispatch issued on a side stream, completed on the main stream by a hook,
