@@ -734,10 +734,24 @@ def main():
             "us_per_kernel_cold_p10_p50_p90": cold_pct,
             "us_per_kernel_cold_read_p10_p50_p90": cold_read_pct,
             "alg_bytes_per_step": ll_bytes,
+            "alg_bytes_per_call": {n: alg_d[n] for n in ("dispatch", "combine")},
             "GB/s_warm": round(ll_bytes / (warm_us * 1e-6) / 1e9, 1)}
         sd["ctx"].close()
         del sd
         torch.cuda.empty_cache()
+
+    if "decode" in line and a.workload == "prefill" and a.step == "forward":
+        # the metric's two sizes side by side: dispatch and combine, us per call
+        def call(us, nbytes):
+            gbs = nbytes / (us * 1e-6) / 1e9
+            return {"us": us, "GB/s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+        dd = line["decode"]
+        line["per_call"] = {
+            "what": ("us per call: 4096 tokens cold (a 1 GiB write before each step; the library's events "
+                     "around each launch), 128 tokens as graph nodes (100 calls captured, replayed)"),
+            "4096_tokens": {n: call(per_kernel[n]["us"], per_kernel[n]["alg_bytes"]) for n in ("dispatch", "combine")},
+            "128_tokens": {n: call(dd["us_per_call_graph"][n], dd["alg_bytes_per_call"][n])
+                           for n in ("dispatch", "combine")}}
 
     if not a.profile_only:
         cp = copy_reference(torch)

@@ -60,3 +60,18 @@ def test_bench_line_backward_step():
     d = run_bench("--step", "backward", *QUICK)
     check_line(d, 5, 2)
     assert set(d["kernels"]) == {"dispatch_bwd", "combine_bwd"}
+
+
+def test_bench_line_per_call_at_both_sizes():
+    """With the decode side measurement on, the line carries dispatch and
+    combine us per call at 4096 and at 128 tokens, with their rates."""
+    d = run_bench("--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--no-backward", "--no-overlap",
+                  "--no-configs")
+    check_line(d, 5, 2)
+    pc = d["per_call"]
+    for size in ("4096_tokens", "128_tokens"):
+        for n in ("dispatch", "combine"):
+            e = pc[size][n]
+            assert e["us"] > 0 and e["GB/s"] > 0 and 0 < e["pct_of_hbm_peak"] < 100, (size, n, e)
+    assert pc["4096_tokens"]["dispatch"]["us"] == d["kernels"]["dispatch"]["us"]
+    assert pc["128_tokens"]["combine"]["us"] == d["decode"]["us_per_call_graph"]["combine"]
