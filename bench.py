@@ -425,7 +425,8 @@ def all_configs(moe, W, torch, flushes, with_oracle=True):
     """Per workload (the layout-reusing step for the contiguous layout, the
     fused low-latency step for the padded one): the step time and algorithmic
     GB/s cold (the headline protocol, a 1 GiB write flush before each step)
-    and warm (back to back), and per kernel the p10/p50/p90 event durations
+    and warm (back to back), the step replayed from a HIP graph (no host
+    launch cost; warm), and per kernel the p10/p50/p90 event durations
     warm and cold: 10 warm-up steps, then 1000 timed steps for the two
     latency-bound workloads and 100 for the others.  With `with_oracle`, also
     the oracle on the same inputs on one host core, layout, dispatch and
@@ -443,6 +444,7 @@ def all_configs(moe, W, torch, flushes, with_oracle=True):
             fn = step_ll
             alg["layout"] = 0
         us = 1e6 * timed(moe, torch, s, steps, 10, fn=fn) / steps
+        us_graph = 1e6 * timed_graph(moe, torch, s, fn)
         cold_ms, _ = timed_cold(moe, torch, s, steps, 10, flushes["cold"], fn=fn)
         us_cold = 1e3 * sum(cold_ms) / len(cold_ms)
         kt = timed_kernels(moe, torch, s, steps, fn=fn)
@@ -454,7 +456,8 @@ def all_configs(moe, W, torch, flushes, with_oracle=True):
                      "us_per_step_cold_p10_p50_p90": percentiles_us(cold_ms),
                      "GB/s_cold": round(b / (us_cold * 1e-6) / 1e9, 1),
                      "pct_of_hbm_peak_cold": round(100 * b / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                     "us_per_step": round(us, 2), "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                     "us_per_step": round(us, 2), "us_per_step_graph": round(us_graph, 2),
+                     "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                      "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
                      "steps": steps, "kernels": kernel_table(kt, alg, cold=kt_cold)}
         if with_oracle:

@@ -584,13 +584,15 @@ def test_ll_fused_irregular_routing(gpu):
 
 
 # ---------------------------------------------------------------- HIP graph capture
-@pytest.mark.parametrize("name,reuse", [("decode", False), ("prefill", True)])
-def test_graph_capture_replays_match_eager(gpu, name, reuse):
+@pytest.mark.parametrize("name,reuse,prefetch", [("decode", False, False), ("prefill", True, False),
+                                                  ("prefill", True, True)])
+def test_graph_capture_replays_match_eager(gpu, name, reuse, prefetch):
     """The calls only enqueue kernels (no allocation, no memset, no sync), so a
     step captures into a HIP graph.  Replay it several times, with eager work
     and a synchronisation between replays, and check every replay against the
-    eager results."""
-    c = small_cfg(name)
+    eager results.  prefetch: the layout call also reads x (2.7 MB of rows, so
+    its extra workgroups run)."""
+    c = small_cfg(name, H=2048 if prefetch else 512)
     T = 128 if name == "decode" else 700
     d = W.make(name, T=T)
     c["max_tokens"] = T
@@ -609,7 +611,7 @@ def test_graph_capture_replays_match_eager(gpu, name, reuse):
 
     def step():
         if reuse:
-            gpu.moe_dispatch_layout(ctx, idx, cnt_e, cnt_r, in_rank)
+            gpu.moe_dispatch_layout(ctx, idx, cnt_e, cnt_r, in_rank, x=x if prefetch else None)
         gpu.moe_dispatch(ctx, x, idx, reuse_layout=reuse, bufs=bufs, handle=h)
         gpu.moe_combine(ctx, y, w, h, out=out)
 
