@@ -126,8 +126,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // row stores the dispatch is fastest with one chunk per lane (5-11% ahead of
 // whole rows per wavefront on the prefill, grouped and skewed shapes).  The
 // combine (and the dispatch backward, the same kernel) takes two: one chunk
-// per lane is 1-2% faster with warm caches but 12-15% slower when the caches
-// hold other kernels' dirty lines.  The combine backward wants at most 8
+// per lane is within 1% on the prefill shape in every cache state and 2%
+// faster on skewed shapes; four are 7-20% slower.  The combine backward wants at most 8
 // slices per token (one chunk per lane up to 512 chunks per row, then two),
 // which is faster in every cache state measured.
 void row_split(int64_t T, int64_t nchunk, int forced, int cap, int* chunks, int* nslices) {
