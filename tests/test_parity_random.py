@@ -1,8 +1,9 @@
 """GPU parity over seeded random configurations: expert and rank counts,
 top-k, hidden size, token count, quantisation, layout, layout reuse, source
 rank and workgroup cap drawn together, with empty slots, repeated experts in
-a row and bad expert ids, forward (layout, dispatch, combine) and backward (dispatch backward,
-combine backward) against the oracle.  Same bar as the targeted tests."""
+a row and bad expert ids, forward (layout, in every other case reading x as
+well, dispatch, combine) and backward (dispatch backward, combine backward)
+against the oracle.  Same bar as the targeted tests."""
 import numpy as np
 import pytest
 
@@ -12,7 +13,7 @@ from test_parity_backward import run_backward
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 40
 _MAX_EXPERT_OUT_BYTES = 4 << 30      # keeps every case's buffers small on the device
 
 
@@ -68,7 +69,8 @@ def test_random_config(gpu, case):
     x, idx, w = _inputs(c)
     tag = "random-%d (E=%d R=%d k=%d H=%d T=%d q=%d ll=%d)" % (case, c["E"], c["R"], c["k"], c["H"], c["T"],
                                                                c["quant"], c["layout"])
+    # every other case gives the layout call x too (its launch then also reads the rows)
     run_case(gpu, c, x, idx, w, reuse=c["reuse"], max_tokens=c["max_tokens"], src_rank=c["s0"], tag=tag,
-             max_workgroups=c["max_wg"])
+             max_workgroups=c["max_wg"], prefetch=case % 2 == 1)
     run_backward(gpu, c, x, idx, w, max_tokens=c["max_tokens"], tag=tag, max_workgroups=c["max_wg"],
                  src_rank=c["s0"])
