@@ -406,8 +406,7 @@ __device__ __forceinline__ ChunkState chunk_state(int64_t gi, int64_t nchunk) {
 // system scope (sc0 sc1 nt).  Measured on MI355X against plain non-temporal
 // stores (dispatch, after a 1 GiB write flush): prefill 180 -> 176 us, skewed
 // 118 -> 115 us, grouped fp8 81 -> 80 us, and the decode step 10.65 -> 9.8 us
-// graph-replayed (the launch ends with fewer dirty lines to write back).
-// System scope without nt makes the rows allocate in the Infinity Cache:
+// graph-replayed.  System scope without nt makes the rows allocate in the Infinity Cache:
 // prefill 171 us, but skewed 124 us and grouped fp8 98 us, so nt stays.
 constexpr int kStoreRows = 0x13;   // sc0 sc1 nt
 
